@@ -1,0 +1,185 @@
+/*
+ * dsl.h -- one DeepSeek-V4.1-style decode layer (M <= 48 rows) as one persistent
+ * HIP launch on MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What a step computes ("Mono decode layer for DeepSeek-V4.1-Flash on MI355X",
+ * vLLM PR 60397, Purpose, launch table rows K1 and K2):
+ *   attention front  RMSNorm(x) -> MXFP8 quantize -> wqkv -> q/kv RMSNorm ->
+ *                    fp8 KV-record insert -> MXFP8 quantize -> wq_b
+ *   attention back   sliding-window split attention -> log-sum-exp combine ->
+ *                    wo_a -> wo_b (each MXFP8, 32x32 E8M0 weight tiles)
+ *   MoE              f32 router logits -> top-k (softmax over the selected k) ->
+ *                    FP8 shared expert + MXFP4 routed experts, clamped SwiGLU ->
+ *                    fixed-order f32 combine
+ * with a pre-norm residual: hres = bf16(x + attn), out = bf16(hres + MoE(RMSNorm(hres))).
+ * The tensor-parallel all-reduces of the pages are not part of this library.
+ *
+ * Conventions
+ *   - Every call returns 0 or a negative DSL_E* code; dsl_last_error() gives the
+ *     message (thread-local).  All argument checks run on the host before any
+ *     launch, so every refusal is testable without a GPU.
+ *   - Step calls are asynchronous on the given stream (NULL = the null stream).
+ *     A device-side failure (a grid barrier that never completed, a slot outside
+ *     the cache) is reported by dsl_layer_health().
+ *   - The caller owns x, out, the weights, the KV caches and the tables; the
+ *     handle owns its sync buffer and one scratch buffer per step width.  The
+ *     weights are read in place, never copied ("Design": weights are read in
+ *     place with no second copy).  A handle is not thread-safe, and two steps of
+ *     one handle must not run concurrently on different streams.
+ *   - Step widths M are 1..dims.max_rows (max_rows <= 48: "Scope", decode only,
+ *     at most 48 rows).  Each width gets its own scratch at its first step
+ *     ("Design": a scratch per step width); dsl_layer_reserve() allocates it
+ *     ahead of time (call it before capturing a step into a HIP graph).
+ *   - positions[r] = -1 marks a pad row: no KV write, ids -1, weights 0 and zero
+ *     rows in every output ("Test Plan": the kernels skip pad rows, whose slot
+ *     is -1).  Rows of one request must have distinct positions.
+ */
+#ifndef DSL_H
+#define DSL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSL_OK 0
+#define DSL_EINVAL (-1)       /* a null pointer, a bad stride, a size out of range  */
+#define DSL_EUNSUPPORTED (-2) /* dims or widths the kernels do not cover; not gfx950;
+                                 fewer CUs than one co-resident grid needs        */
+#define DSL_ENOMEM (-3)       /* device allocation failed                            */
+#define DSL_EHIP (-4)         /* a HIP runtime call failed (message has the code)    */
+#define DSL_EDEVICE (-5)      /* dsl_layer_health: a device-side fault was recorded  */
+
+#define DSL_MAX_ROWS 48
+#define DSL_MAX_LAYERS 4
+
+/* Layer dimensions.  All sizes in elements.  Constraints checked by
+ * dsl_layer_build: hidden, q_rank, o_rank, inter, shared_inter and
+ * n_heads*head_dim positive multiples of 128 (the kernels stream K in steps of
+ * 128; the shared expert has 128x128 scale blocks); head_dim in {64, 128, 256,
+ * 512}; 1 <= n_experts <= 128; 1 <= top_k <= min(8, n_experts);
+ * 1 <= max_rows <= 48; 1 <= n_layers <= DSL_MAX_LAYERS; window >= 1;
+ * swa_width >= 0; kv_block >= 1.  Other values: DSL_EUNSUPPORTED or DSL_EINVAL. */
+typedef struct {
+  int32_t hidden, n_heads, head_dim, q_rank, o_rank;
+  int32_t window;      /* causal sliding window W; a row at position p sees
+                          positions [max(0, p-W+1), p] of its request          */
+  int32_t swa_width;   /* 0 = causal window mode; > 0 = index-table mode: each
+                          row attends to the slots of its key_table row (the draft
+                          layers' non-causal rows, 192 wide for window 128 and 5
+                          drafts: "Mono decode for the DSpark draft layers",
+                          vLLM PR 62131, Details)                               */
+  int32_t n_experts, top_k, inter, shared_inter;
+  int32_t kv_block;    /* B, tokens per cache block                             */
+  int32_t max_rows;    /* largest step width                                    */
+  int32_t n_layers;    /* chained layers per step (3 for the draft model)       */
+  float norm_eps;      /* RMSNorm epsilon (1e-6)                                */
+  float swiglu_limit;  /* SwiGLU clamp (7.0)                                    */
+} dsl_dims;
+
+/* Device pointers to one layer's weights, caller-owned, read in place; they must
+ * stay valid until dsl_layer_destroy.  Formats ("Design" and "Layout"):
+ *   norms          f32 gammas: attn_norm, ffn_norm [hidden]; q_norm [q_rank];
+ *                  kv_norm [head_dim]
+ *   MXFP8 linears  e4m3 row-major [N][K] plus one E8M0 byte per 32x32 tile,
+ *                  row-major [N/32][K/32]:
+ *                  wqkv [q_rank+head_dim][hidden] (q latent rows first),
+ *                  wq_b [n_heads*head_dim][q_rank], wo_a [o_rank][n_heads*head_dim],
+ *                  wo_b [hidden][o_rank]
+ *   router         f32 [n_experts][hidden]
+ *   shared expert  e4m3 row-major, f32 scale per 128x128 block:
+ *                  sh_w13 [2*shared_inter][hidden] (gate rows, then up rows),
+ *                  sh_w13_s [2*shared_inter/128][hidden/128];
+ *                  sh_wd [hidden][shared_inter], sh_wd_s [hidden/128][shared_inter/128]
+ *   routed experts e2m1 nibbles, low nibble = even k, one E8M0 per 32 along k:
+ *                  ex_w13 [n_experts][2*inter][hidden/2], ex_w13_s [n_experts][2*inter][hidden/32]
+ *                  ex_wd  [n_experts][hidden][inter/2],   ex_wd_s  [n_experts][hidden][inter/32]
+ * All pointers 16-byte aligned. */
+typedef struct {
+  const float *attn_norm, *q_norm, *kv_norm, *ffn_norm;
+  const uint8_t *wqkv, *wqkv_s, *wq_b, *wq_b_s, *wo_a, *wo_a_s, *wo_b, *wo_b_s;
+  const float *w_router;
+  const uint8_t *sh_w13;
+  const float *sh_w13_s;
+  const uint8_t *sh_wd;
+  const float *sh_wd_s;
+  const uint8_t *ex_w13, *ex_w13_s, *ex_wd, *ex_wd_s;
+} dsl_weights;
+
+/* One layer's block-paged fp8 KV cache, written in place at each live row's slot.
+ * Record (RECORD = head_dim + 16 bytes): head_dim e4m3 codes, then the f32 scale
+ * s = amax/448, then 12 zero bytes.  The cache is a [blocks][B][RECORD] view whose
+ * block stride must be at least B*RECORD ("[SpecializedDecode] review thread",
+ * vLLM PR 61311: the stride check) and a multiple of 16.  The slot of position p
+ * of request q is block_table[q][p / B] * B + p % B.  All pointers are device
+ * pointers. */
+typedef struct {
+  uint8_t *base;
+  int64_t block_stride;       /* bytes                                           */
+  int64_t n_blocks;           /* physical blocks in the view (slot bound)        */
+  const int32_t *block_table; /* [n_req][max_blocks] physical block ids          */
+  int32_t max_blocks;
+  int32_t n_req;              /* rows of block_table (request index bound)       */
+  const int32_t *row_req;     /* [M] request index of each row                   */
+  const int32_t *key_table;   /* [M][swa_width] physical slots or -1 (index-table
+                                 mode only; NULL otherwise)                       */
+} dsl_kv;
+
+/* Optional intermediate outputs of the last layer of a step (NULL = not written). */
+typedef struct {
+  void *attn_out;     /* bf16 [M][hidden]: attention branch output bf16(a)       */
+  void *hres;         /* bf16 [M][hidden]: residual after attention             */
+  void *moe_in;       /* bf16 [M][hidden]: RMSNorm_ffn(hres), the MoE input      */
+  void *moe_out;      /* bf16 [M][hidden]: MoE branch output                     */
+  int32_t *topk_ids;  /* [M][top_k], emitted in descending logit order           */
+  float *topk_w;      /* [M][top_k]                                              */
+  float *logits;      /* [M][n_experts] f32 router logits                        */
+} dsl_taps;
+
+typedef struct dsl_layer dsl_layer;
+
+/* Validate dims, query the current device (must be gfx950 with enough CUs for the
+ * co-resident grid), copy the n_layers weight descriptors (not the weights) and
+ * allocate the sync buffer.  weights points to dims->n_layers descriptors.
+ * On success *out receives the handle.  Errors: DSL_EINVAL, DSL_EUNSUPPORTED,
+ * DSL_ENOMEM, DSL_EHIP. */
+int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer **out);
+
+/* Allocate the scratch of width M now (otherwise the first step of that width does). */
+int dsl_layer_reserve(dsl_layer *layer, int32_t M);
+
+/* One decode step over n_layers chained layers: x bf16 [M][hidden] in, out bf16
+ * [M][hidden].  kv points to n_layers cache descriptors (their tables may be
+ * shared); positions [M] int32 device array.  taps may be NULL. */
+int dsl_decode_step(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_kv *kv,
+                    const int32_t *positions, void *out_bf16, const dsl_taps *taps,
+                    void *hip_stream);
+
+/* The attention half of layer 0 only: attn_out = bf16(a), no residual add.  Writes
+ * the KV records like a full step. */
+int dsl_attn_step(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_kv *kv,
+                  const int32_t *positions, void *attn_out_bf16, void *hip_stream);
+
+/* The MoE of layer 0 only, on an already normalized input u bf16 [M][hidden]:
+ * moe_out = bf16(shared + sum_j w_j expert_j).  topk_ids [M][top_k] and topk_w
+ * [M][top_k] may be NULL. */
+int dsl_moe_step(dsl_layer *layer, const void *u_bf16, int32_t M, void *moe_out_bf16,
+                 int32_t *topk_ids, float *topk_w, void *hip_stream);
+
+/* Synchronizes nothing; reads the device health word after the caller has
+ * synchronized.  0 = healthy; DSL_EDEVICE after a recorded device fault (the word
+ * is then cleared and the handle's sync state reset). */
+int dsl_layer_health(dsl_layer *layer);
+
+/* Grid the persistent launch uses (blocks, threads per block); for reports. */
+int dsl_layer_grid(const dsl_layer *layer, int32_t *blocks, int32_t *threads);
+
+void dsl_layer_destroy(dsl_layer *layer);
+
+const char *dsl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSL_H */

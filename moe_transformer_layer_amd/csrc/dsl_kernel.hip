@@ -1,0 +1,1000 @@
+// The decode layer as one persistent cooperative launch on gfx950, and the host
+// runtime behind the C ABI of include/dsl.h.
+//
+// One launch runs, per layer, the stages of "Mono decode layer for
+// DeepSeek-V4.1-Flash on MI355X" (vLLM PR 60397), Purpose, launch table (K1 and
+// K2 without the tensor-parallel all-reduces), with a grid barrier between
+// dependent stages.  Three draft layers chain inside the same launch ("Mono
+// decode for the DSpark draft layers", vLLM PR 62131, Details).  Routed-expert
+// work is claimed from a device task queue (atomic counters in the handle's sync
+// buffer), everything else is split statically over the grid's waves.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "dsl_stages.h"
+
+namespace dsl {
+
+// ============================================================== attention front
+
+// RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values)
+__device__ void st_attn_norm(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *xin) {
+  for (int m = cx.gw; m < p.M; m += cx.nw) {
+    const uint16_t *row = xin + (size_t)m * p.h;
+    auto load4 = [&](int k) {
+      const v2u v = *reinterpret_cast<const v2u *>(row + k);
+      return make_float4(bf16_to_f32(v[0] & 0xFFFFu), bf16_to_f32(v[0] >> 16), bf16_to_f32(v[1] & 0xFFFFu),
+                         bf16_to_f32(v[1] >> 16));
+    };
+    wave_row_mxq(load4, p.h, w.attn_norm, p.eps, p.s.xb + (size_t)m * p.h, cx.lane);
+  }
+}
+
+// Physical record of a slot, or null (with a recorded fault) if the slot is outside
+// the cache view.
+__device__ __forceinline__ uint8_t *record_ptr(const Params &p, const dsl_kv &kv, int64_t slot) {
+  const int64_t blk = slot / p.B;
+  if (slot < 0 || blk >= kv.n_blocks) {
+    __hip_atomic_fetch_or(&p.sync->health, (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return nullptr;
+  }
+  return kv.base + blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
+}
+
+// Slot of token position t of request req through the block table, or -1.
+__device__ __forceinline__ int64_t slot_of(const Params &p, const dsl_kv &kv, int req, int t) {
+  const int lb = t / p.B;
+  if (req < 0 || req >= kv.n_req || t < 0 || lb >= kv.max_blocks) return -1;
+  const int blk = kv.block_table[(size_t)req * kv.max_blocks + lb];
+  return blk < 0 ? -1 : (int64_t)blk * p.B + (t - lb * p.B);
+}
+
+// q latent: sum the split-K partials, RMSNorm, MXFP8.  kv latent: RMSNorm, then the
+// fp8 record (codes e4m3(v / s), s = amax / 448) written at the row's slot.
+__device__ void st_qkv_post(const Params &p, const Ctx &cx, const dsl_weights &w, const dsl_kv &kv) {
+  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv;
+  const size_t pstride = (size_t)p.M * N;
+  for (int m = cx.gw; m < p.M; m += cx.nw) {
+    const float *base = p.s.p_qkv + (size_t)m * N;
+    auto load4 = [&](int k) {
+      float4 a = *reinterpret_cast<const float4 *>(base + k);
+      for (int ks = 1; ks < nks; ks++) {
+        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      return a;
+    };
+    wave_row_mxq(load4, p.qr, w.q_norm, p.eps, p.s.qb + (size_t)m * p.qr, cx.lane);
+    const int pos = p.pos[m];
+    if (pos < 0) continue;  // pad row: no KV write
+    const int D = p.D;
+    float v[2][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const int k = 4 * cx.lane + 256 * c;
+      if (k < D) {
+        const float4 a = load4(p.qr + k);
+        v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
+      } else {
+        v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++) ss += v[c][e] * v[c][e];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + p.eps);
+    float am = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const int k = 4 * cx.lane + 256 * c;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        v[c][e] = k < D ? v[c][e] * r * w.kv_norm[k + e] : 0.f;
+        am = fmaxf(am, fabsf(v[c][e]));
+      }
+    }
+    am = wave_max(am);
+    const float sc = am / 448.0f;
+    uint8_t *rec = record_ptr(p, kv, slot_of(p, kv, kv.row_req[m], pos));
+    if (!rec) continue;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const int k = 4 * cx.lane + 256 * c;
+      if (k < D) {
+        uint32_t code = 0;
+        if (sc > 0.f) {
+#pragma unroll
+          for (int e = 0; e < 4; e++) code |= f32_to_e4m3(v[c][e] / sc) << (8 * e);
+        }
+        *reinterpret_cast<uint32_t *>(rec + k) = code;
+      }
+    }
+    if (cx.lane == 0) st16(rec + D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
+  }
+}
+
+// ============================================================== attention
+
+template <int V>
+__device__ __forceinline__ void load_codes(const uint8_t *p, float out[V]) {
+  if constexpr (V == 8) {
+    const v2u c = *reinterpret_cast<const v2u *>(p);
+    const v2f a = cvt_fp8x2_f32<false>(c[0]), b = cvt_fp8x2_f32<true>(c[0]);
+    const v2f d = cvt_fp8x2_f32<false>(c[1]), e = cvt_fp8x2_f32<true>(c[1]);
+    out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+    out[4] = d[0]; out[5] = d[1]; out[6] = e[0]; out[7] = e[1];
+  } else if constexpr (V == 4) {
+    const uint32_t c = *reinterpret_cast<const uint32_t *>(p);
+    const v2f a = cvt_fp8x2_f32<false>(c), b = cvt_fp8x2_f32<true>(c);
+    out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+  } else if constexpr (V == 2) {
+    const uint32_t c = *reinterpret_cast<const uint16_t *>(p);
+    const v2f a = cvt_fp8x2_f32<false>(c);
+    out[0] = a[0]; out[1] = a[1];
+  } else {
+    out[0] = e4m3_to_f32(*p);
+  }
+}
+
+// One (row, head, split): scores q . k / sqrt(D) over up to 32 keys of the row's key set,
+// with k = v = scale * e4m3(codes) of the record; partial max, sum of exponentials and
+// exponential-weighted sum of values.  Lane l holds dims [V*l, V*l + V).
+template <int V>
+__device__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane) {
+  const int D = p.D, H = p.H;
+  const int pos = p.pos[m];
+  const size_t item = ((size_t)m * H + hh) * p.S + sp;
+  float *o_out = p.s.att_o + item * D;
+  float *ml = p.s.att_ml + item * 2;
+  int nk, lo = 0;
+  if (p.swa > 0) {
+    nk = p.swa;
+  } else {
+    lo = pos - p.W + 1 < 0 ? 0 : pos - p.W + 1;
+    nk = pos - lo + 1;
+  }
+  const int j0 = sp * kSplitKeys, j1 = min(nk, j0 + kSplitKeys);
+  const int nks = p.qr / p.pl.kc_qb;
+  const size_t qstride = (size_t)p.M * H * D;
+  const float *qp = p.s.p_q + (size_t)m * H * D + (size_t)hh * D + lane * V;
+  float q[V];
+#pragma unroll
+  for (int v = 0; v < V; v++) q[v] = 0.f;
+  for (int ks = 0; ks < nks; ks++) {
+#pragma unroll
+    for (int v = 0; v < V; v++) q[v] += qp[ks * qstride + v];
+  }
+  const int req = kv.row_req[m];
+  auto rec_of = [&](int j) -> const uint8_t * {
+    int64_t slot;
+    if (p.swa > 0) {
+      slot = kv.key_table[(size_t)m * p.swa + j];
+      if (slot < 0) return nullptr;
+    } else {
+      slot = slot_of(p, kv, req, lo + j);
+    }
+    return record_ptr(p, kv, slot);
+  };
+  float my = -INFINITY;
+  for (int j = j0; j < j1; j++) {
+    const uint8_t *rec = rec_of(j);
+    if (!rec) continue;
+    float c[V];
+    load_codes<V>(rec + lane * V, c);
+    const float sc = *reinterpret_cast<const float *>(rec + D);
+    float d = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; v++) d += q[v] * c[v];
+    d = wave_sum(d) * sc * p.attn_scale;
+    if (lane == j - j0) my = d;
+  }
+  const float mx = wave_max(my);
+  const float pj = my == -INFINITY ? 0.f : expf(my - mx);
+  const float l = wave_sum(pj);
+  float o[V];
+#pragma unroll
+  for (int v = 0; v < V; v++) o[v] = 0.f;
+  for (int j = j0; j < j1; j++) {
+    const float pw = __shfl(pj, j - j0, kWave);
+    if (pw == 0.f) continue;
+    const uint8_t *rec = rec_of(j);
+    if (!rec) continue;
+    float c[V];
+    load_codes<V>(rec + lane * V, c);
+    const float f = pw * *reinterpret_cast<const float *>(rec + D);
+#pragma unroll
+    for (int v = 0; v < V; v++) o[v] += f * c[v];
+  }
+#pragma unroll
+  for (int v = 0; v < V; v++) o_out[lane * V + v] = o[v];
+  if (lane == 0) {
+    ml[0] = mx;
+    ml[1] = l;
+  }
+}
+
+template <int V>
+__device__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv) {
+  const int T = p.M * p.H * p.S;
+  for (int t = cx.gw; t < T; t += cx.nw) {
+    const int m = t / (p.H * p.S), rem = t - m * p.H * p.S;
+    const int hh = rem / p.S, sp = rem - hh * p.S;
+    if (p.pos[m] < 0) continue;
+    attn_item<V>(p, kv, m, hh, sp, cx.lane);
+  }
+}
+
+// Log-sum-exp combine of the splits of one (row, head), then MXFP8 of the output
+// (32-blocks span 32/V lanes).  Pad rows give zeros.
+template <int V>
+__device__ void st_combine_v(const Params &p, const Ctx &cx) {
+  const int T = p.M * p.H, D = p.D, S = p.S;
+  for (int t = cx.gw; t < T; t += cx.nw) {
+    const int m = t / p.H, hh = t - m * p.H;
+    float o[V];
+#pragma unroll
+    for (int v = 0; v < V; v++) o[v] = 0.f;
+    if (p.pos[m] >= 0) {
+      const size_t item0 = ((size_t)m * p.H + hh) * S;
+      const float *ml = p.s.att_ml + item0 * 2;
+      float mx = -INFINITY;
+      for (int s = 0; s < S; s++) mx = fmaxf(mx, ml[2 * s]);
+      float L = 0.f;
+      for (int s = 0; s < S; s++) {
+        if (!(ml[2 * s + 1] > 0.f)) continue;
+        const float e = expf(ml[2 * s] - mx);
+        L += ml[2 * s + 1] * e;
+        const float *os = p.s.att_o + (item0 + s) * D + cx.lane * V;
+#pragma unroll
+        for (int v = 0; v < V; v++) o[v] += os[v] * e;
+      }
+      if (L > 0.f) {
+#pragma unroll
+        for (int v = 0; v < V; v++) o[v] = o[v] / L;
+      }
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; v++) am = fmaxf(am, fabsf(o[v]));
+    am = group_max<32 / V>(am);
+    const uint32_t X = mx_e4m3_exponent(am);
+    const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
+    uint16_t *dst = p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + cx.lane * V;
+#pragma unroll
+    for (int v = 0; v < V; v++) dst[v] = (uint16_t)f32_to_bf16(e4m3_to_f32(f32_to_e4m3(o[v] * inv)) * sc);
+  }
+}
+
+// wo_a output: sum the split-K partials, then MXFP8
+__device__ void st_t_quant(const Params &p, const Ctx &cx) {
+  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa;
+  const size_t pstride = (size_t)p.M * N;
+  for (int m = cx.gw; m < p.M; m += cx.nw) {
+    const float *base = p.s.p_t + (size_t)m * N;
+    auto load4 = [&](int k) {
+      float4 a = *reinterpret_cast<const float4 *>(base + k);
+      for (int ks = 1; ks < nks; ks++) {
+        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      return a;
+    };
+    wave_row_mxq(load4, N, nullptr, 0.f, p.s.tb + (size_t)m * N, cx.lane);
+  }
+}
+
+// wo_b output a (sum of partials).  Attention-only steps write bf16(a).  Full steps:
+// hres = bf16(x + a), u = bf16(RMSNorm_ffn(hres)).  Pad rows give zeros.
+__device__ void st_ffn_norm(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *xin, bool last) {
+  const int h = p.h, nks = p.orr / p.pl.kc_ob;
+  const size_t pstride = (size_t)p.M * h;
+  const int nb = h >> 5;
+  for (int m = cx.gw; m < p.M; m += cx.nw) {
+    const bool live = p.pos[m] >= 0;
+    const float *base = p.s.p_a + (size_t)m * h;
+    const uint16_t *xr = xin + (size_t)m * h;
+    auto a4 = [&](int k) {
+      float4 a = *reinterpret_cast<const float4 *>(base + k);
+      for (int ks = 1; ks < nks; ks++) {
+        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      return a;
+    };
+    auto hres4 = [&](int k, float hr[4]) {
+      const float4 a = a4(k);
+      const v2u xv = *reinterpret_cast<const v2u *>(xr + k);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+      const float xf[4] = {bf16_to_f32(xv[0] & 0xFFFFu), bf16_to_f32(xv[0] >> 16), bf16_to_f32(xv[1] & 0xFFFFu),
+                           bf16_to_f32(xv[1] >> 16)};
+#pragma unroll
+      for (int e = 0; e < 4; e++) hr[e] = live ? bf16_to_f32(f32_to_bf16(xf[e] + av[e])) : 0.f;
+    };
+    auto pack = [](const float f[4]) {
+      return v2u{f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16), f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16)};
+    };
+    if (p.mode == kModeAttn) {
+      for (int k = cx.lane * 4; k < h; k += 4 * kWave) {
+        const float4 a = a4(k);
+        const float f[4] = {live ? a.x : 0.f, live ? a.y : 0.f, live ? a.z : 0.f, live ? a.w : 0.f};
+        *reinterpret_cast<v2u *>(p.out + (size_t)m * h + k) = pack(f);
+      }
+      continue;
+    }
+    float ss = 0.f;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      const int blk = b0 + (cx.lane >> 3);
+      if (blk >= nb) continue;
+      const int k = blk * 32 + (cx.lane & 7) * 4;
+      float hr[4];
+      hres4(k, hr);
+#pragma unroll
+      for (int e = 0; e < 4; e++) ss += hr[e] * hr[e];
+      if (last) {
+        if (p.taps.hres) *reinterpret_cast<v2u *>((uint16_t *)p.taps.hres + (size_t)m * h + k) = pack(hr);
+        if (p.taps.attn_out) {
+          const float4 a = a4(k);
+          const float f[4] = {live ? a.x : 0.f, live ? a.y : 0.f, live ? a.z : 0.f, live ? a.w : 0.f};
+          *reinterpret_cast<v2u *>((uint16_t *)p.taps.attn_out + (size_t)m * h + k) = pack(f);
+        }
+      }
+      *reinterpret_cast<v2u *>(p.s.hres + (size_t)m * h + k) = pack(hr);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)h + p.eps);
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      const int blk = b0 + (cx.lane >> 3);
+      if (blk >= nb) continue;
+      const int k = blk * 32 + (cx.lane & 7) * 4;
+      float hr[4], uu[4];
+      hres4(k, hr);
+#pragma unroll
+      for (int e = 0; e < 4; e++) uu[e] = live ? hr[e] * r * w.ffn_norm[k + e] : 0.f;
+      const v2u pk = pack(uu);
+      *reinterpret_cast<v2u *>(p.s.u + (size_t)m * h + k) = pk;
+      if (last && p.taps.moe_in) *reinterpret_cast<v2u *>((uint16_t *)p.taps.moe_in + (size_t)m * h + k) = pk;
+    }
+  }
+}
+
+// ============================================================== MoE
+
+// f32 router logits of one expert for all rows: lane-strided dot products, then a wave sum
+__device__ void router_task(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e, int lane) {
+  constexpr int MR = DSL_MAX_ROWS;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; m++) acc[m] = 0.f;
+  const float *wrow = Wr + (size_t)e * p.h;
+  for (int k = lane * 4; k < p.h; k += 4 * kWave) {
+    const float4 w4 = *reinterpret_cast<const float4 *>(wrow + k);
+#pragma unroll
+    for (int m = 0; m < MR; m++) {
+      if (m < p.M) {
+        const v2u uv = *reinterpret_cast<const v2u *>(u + (size_t)m * p.h + k);
+        acc[m] += w4.x * bf16_to_f32(uv[0] & 0xFFFFu) + w4.y * bf16_to_f32(uv[0] >> 16) +
+                  w4.z * bf16_to_f32(uv[1] & 0xFFFFu) + w4.w * bf16_to_f32(uv[1] >> 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; m++) {
+    if (m < p.M) {
+      const float s = wave_sum(acc[m]);
+      if (lane == 0) p.s.logits[(size_t)m * p.E + e] = s;
+    }
+  }
+}
+
+// Router logits (E tasks) and the shared expert's gate/up partials, together: both
+// read only the MoE input.
+__device__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
+  const int TR = p.E;
+  const int Nsh = 2 * p.Is;
+  const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
+  for (int t = cx.gw; t < TR + TS; t += cx.nw) {
+    if (t < TR)
+      router_task(p, w.w_router, u, t, cx.lane);
+    else
+      linear_task<kW8B128>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u, p.M,
+                           p.s.p_sh);
+  }
+}
+
+// Top-k of every live row (ties to the lower id, descending order, weights = softmax of
+// the selected logits), then the distinct-expert list and the (row, slot) -> pair map
+// ordered by expert id.  Every block builds the same routing in its own LDS.
+__device__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
+  const int k = p.k, E = p.E;
+  for (int e = threadIdx.x; e < 128; e += kThreads) R.cnt[e] = 0;
+  __syncthreads();
+  for (int m = cx.wave; m < p.M; m += kWavesPerBlock) {
+    const bool live = all_live || p.pos[m] >= 0;
+    if (!live) {
+      if (cx.lane < k) {
+        R.ids[m * k + cx.lane] = -1;
+        R.w[m * k + cx.lane] = 0.f;
+      }
+      continue;
+    }
+    const float *lg = p.s.logits + (size_t)m * E;
+    float l0 = cx.lane < E ? lg[cx.lane] : -INFINITY;
+    float l1 = cx.lane + 64 < E ? lg[cx.lane + 64] : -INFINITY;
+    int myid = -1;
+    float myval = -INFINITY;
+    for (int j = 0; j < k; j++) {
+      float bv;
+      int bi;
+      if (l0 >= l1) {
+        bv = l0; bi = cx.lane;
+      } else {
+        bv = l1; bi = cx.lane + 64;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov; bi = oi;
+        }
+      }
+      if (cx.lane == j) {
+        myid = bi; myval = bv;
+      }
+      if (bi == cx.lane) l0 = -INFINITY;
+      if (bi == cx.lane + 64) l1 = -INFINITY;
+    }
+    const float top = __shfl(myval, 0, kWave);
+    const float ev = cx.lane < k ? expf(myval - top) : 0.f;
+    const float sum = wave_sum(ev);
+    if (cx.lane < k) {
+      R.ids[m * k + cx.lane] = myid;
+      R.w[m * k + cx.lane] = ev / sum;
+      atomicAdd(&R.cnt[myid], 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0, nd = 0;
+    for (int e = 0; e < E; e++) {
+      R.start[e] = acc;
+      if (R.cnt[e]) {
+        R.list[nd++] = e;
+        acc += R.cnt[e];
+      }
+    }
+    R.nd = nd;
+  }
+  __syncthreads();
+  const int P = p.M * k;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    if (!R.cnt[e]) continue;
+    int r = 0;
+    for (int t = 0; t < P; t++) {
+      if (R.ids[t] == e) {
+        R.pair[t] = R.start[e] + r;
+        R.pair_row[R.start[e] + r] = t / k;
+        r++;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Shared SwiGLU over all (row, column): z = bf16(swiglu_clamp(gate, up))
+__device__ void st_shared_swiglu(const Params &p, bool all_live) {
+  const int Is = p.Is, nks = p.h / p.pl.kc_sh13;
+  const size_t pstride = (size_t)p.M * 2 * Is;
+  const int total = p.M * Is;
+  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    const int m = idx / Is, n = idx - m * Is;
+    float z = 0.f;
+    if (all_live || p.pos[m] >= 0) {
+      const float *b = p.s.p_sh + (size_t)m * 2 * Is;
+      float g = 0.f, u = 0.f;
+      for (int ks = 0; ks < nks; ks++) {
+        g += b[ks * pstride + n];
+        u += b[ks * pstride + Is + n];
+      }
+      z = swiglu_clamp(g, u, p.lim);
+    }
+    p.s.zsh[idx] = (uint16_t)f32_to_bf16(z);
+  }
+}
+
+template <int NCG>
+__device__ void routed_gate_up_task(const Params &p, const dsl_weights &w, const Routing &R, const uint16_t *u,
+                                    int e, int p0, int ce, int tile, int lane) {
+  const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
+  const uint8_t *W = w.ex_w13 + (size_t)e * (2 * I) * (h >> 1);
+  const uint8_t *S8 = w.ex_w13_s + (size_t)e * (2 * I) * (h >> 5);
+  const uint16_t *xrow[NCG];
+  bool xok[NCG];
+  v4f acc[2][NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; c++) {
+    const int j = 16 * c + i;
+    xok[c] = j < ce;
+    xrow[c] = u + (size_t)(xok[c] ? R.pair_row[p0 + j] : 0) * h;
+    acc[0][c] = acc[1][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const int n0[2] = {tile * 16, I + tile * 16};
+  bf16_tiles<kW4, 2, NCG>(W, S8, nullptr, h, n0, 0, h, xrow, xok, acc, lane);
+#pragma unroll
+  for (int c = 0; c < NCG; c++) {
+    const int j = 16 * c + i;
+    if (j < ce) {
+      uint16_t *z = p.s.zr + (size_t)(p0 + j) * I + tile * 16 + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; r++) z[r] = (uint16_t)f32_to_bf16(swiglu_clamp(acc[0][c][r], acc[1][c][r], p.lim));
+    }
+  }
+}
+
+template <int NCG>
+__device__ void routed_down_task(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile, int lane) {
+  const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
+  const uint8_t *W = w.ex_wd + (size_t)e * h * (I >> 1);
+  const uint8_t *S8 = w.ex_wd_s + (size_t)e * h * (I >> 5);
+  const uint16_t *xrow[NCG];
+  bool xok[NCG];
+  v4f acc[1][NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; c++) {
+    const int j = 16 * c + i;
+    xok[c] = j < ce;
+    xrow[c] = p.s.zr + (size_t)(p0 + (xok[c] ? j : 0)) * I;
+    acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const int n0[1] = {tile * 16};
+  bf16_tiles<kW4, 1, NCG>(W, S8, nullptr, I, n0, 0, I, xrow, xok, acc, lane);
+#pragma unroll
+  for (int c = 0; c < NCG; c++) {
+    const int j = 16 * c + i;
+    if (j < ce) {
+      float *y = p.s.y + (size_t)(p0 + j) * h + tile * 16 + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; r++) y[r] = acc[0][c][r];
+    }
+  }
+}
+
+// Routed gate/up tasks (selected expert, 16-row tile of gate and of up) from the queue
+__device__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
+                                  const uint16_t *u, unsigned *ctr) {
+  const int tiles = p.I >> 4;
+  const int T = R.nd * tiles;
+  for (;;) {
+    const int t = claim_task(ctr, cx.lane);
+    if (t >= T) break;
+    const int q = t / tiles, tile = t - q * tiles;
+    const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
+    const int ncg = (ce + 15) >> 4;
+    if (ncg == 1)
+      routed_gate_up_task<1>(p, w, R, u, e, p0, ce, tile, cx.lane);
+    else if (ncg == 2)
+      routed_gate_up_task<2>(p, w, R, u, e, p0, ce, tile, cx.lane);
+    else
+      routed_gate_up_task<3>(p, w, R, u, e, p0, ce, tile, cx.lane);
+  }
+}
+
+// Shared down partials (static split), then routed down tasks from the queue
+__device__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R, unsigned *ctr) {
+  const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
+  for (int t = cx.gw; t < TS; t += cx.nw)
+    linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
+  const int tiles = p.h >> 4;
+  const int T = R.nd * tiles;
+  for (;;) {
+    const int t = claim_task(ctr, cx.lane);
+    if (t >= T) break;
+    const int q = t / tiles, tile = t - q * tiles;
+    const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
+    const int ncg = (ce + 15) >> 4;
+    if (ncg == 1)
+      routed_down_task<1>(p, w, e, p0, ce, tile, cx.lane);
+    else if (ncg == 2)
+      routed_down_task<2>(p, w, e, p0, ce, tile, cx.lane);
+    else
+      routed_down_task<3>(p, w, e, p0, ce, tile, cx.lane);
+  }
+}
+
+// m = shared + sum_j w_j y_j in float32 (shared first, slots in emission order);
+// MoE steps write bf16(m), full steps bf16(hres + m).
+__device__ void st_combine_out(const Params &p, const Routing &R, bool moe_mode, bool last, uint16_t *dst) {
+  const int h = p.h, k = p.k, nks = p.Is / p.pl.kc_shd;
+  const size_t pstride = (size_t)p.M * h;
+  const int total = p.M * h;
+  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+    const int m = idx / h, n = idx - m * h;
+    const bool live = moe_mode || p.pos[m] >= 0;
+    float mo = 0.f;
+    if (live) {
+      for (int ks = 0; ks < nks; ks++) mo += p.s.p_shd[ks * pstride + idx];
+      for (int j = 0; j < k; j++) mo = fmaf(R.w[m * k + j], p.s.y[(size_t)R.pair[m * k + j] * h + n], mo);
+    }
+    if (moe_mode) {
+      dst[idx] = live ? (uint16_t)f32_to_bf16(mo) : 0;
+    } else {
+      dst[idx] = live ? (uint16_t)f32_to_bf16(bf16_to_f32(p.s.hres[idx]) + mo) : 0;
+      if (last && p.taps.moe_out) ((uint16_t *)p.taps.moe_out)[idx] = live ? (uint16_t)f32_to_bf16(mo) : 0;
+    }
+  }
+}
+
+// ============================================================== the persistent launch
+
+__global__ void __launch_bounds__(kThreads, 2) dsl_layer_kernel(Params p) {
+  __shared__ Routing R;
+  const Ctx cx = make_ctx();
+  SyncWords *sw = p.sync;
+  const unsigned nb = gridDim.x;
+  if (blockIdx.x == 0 && threadIdx.x < 64)
+    __hip_atomic_store(&sw->tasks[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool moe_mode = p.mode == kModeMoe;
+  for (int l = 0; l < p.n_layers; l++) {
+    const dsl_weights w = p.w[l];
+    const dsl_kv &kv = p.kv[l];
+    const bool last = l == p.n_layers - 1;
+    const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+    if (!moe_mode) {
+      st_attn_norm(p, cx, w, xin);
+      grid_barrier(sw, nb);
+      linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
+      grid_barrier(sw, nb);
+      st_qkv_post(p, cx, w, kv);
+      grid_barrier(sw, nb);
+      linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
+      grid_barrier(sw, nb);
+      switch (p.D) {
+        case 64: st_attention_v<1>(p, cx, kv); break;
+        case 128: st_attention_v<2>(p, cx, kv); break;
+        case 256: st_attention_v<4>(p, cx, kv); break;
+        default: st_attention_v<8>(p, cx, kv); break;
+      }
+      grid_barrier(sw, nb);
+      switch (p.D) {
+        case 64: st_combine_v<1>(p, cx); break;
+        case 128: st_combine_v<2>(p, cx); break;
+        case 256: st_combine_v<4>(p, cx); break;
+        default: st_combine_v<8>(p, cx); break;
+      }
+      grid_barrier(sw, nb);
+      linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
+      grid_barrier(sw, nb);
+      st_t_quant(p, cx);
+      grid_barrier(sw, nb);
+      linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
+      grid_barrier(sw, nb);
+      st_ffn_norm(p, cx, w, xin, last);
+      if (p.mode == kModeAttn) return;
+      grid_barrier(sw, nb);
+    }
+    const uint16_t *u = moe_mode ? p.x : p.s.u;
+    st_router_shared(p, cx, w, u);
+    grid_barrier(sw, nb);
+    build_routing(p, cx, R, moe_mode);
+    if (blockIdx.x == 0 && last) {
+      for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) {
+        if (p.taps.topk_ids) p.taps.topk_ids[t] = R.ids[t];
+        if (p.taps.topk_w) p.taps.topk_w[t] = R.w[t];
+      }
+      if (p.taps.logits)
+        for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) p.taps.logits[t] = p.s.logits[t];
+    }
+    st_shared_swiglu(p, moe_mode);
+    st_routed_gate_up(p, cx, w, R, u, &sw->tasks[2 * l]);
+    grid_barrier(sw, nb);
+    st_down(p, cx, w, R, &sw->tasks[2 * l + 1]);
+    grid_barrier(sw, nb);
+    st_combine_out(p, R, moe_mode, last, last ? p.out : p.s.xin);
+    if (!last) grid_barrier(sw, nb);
+  }
+}
+
+}  // namespace dsl
+
+// ============================================================== host runtime
+
+using namespace dsl;
+
+struct WidthScratch {
+  void *buf = nullptr;
+  size_t bytes = 0;
+  Scratch s{};
+};
+
+struct dsl_layer {
+  dsl_dims d{};
+  int dev = 0, cus = 0, grid = 0, bpc = 0, S = 1;
+  Plan plan{};
+  dsl_weights *dw = nullptr;  // device copy of the weight descriptors
+  SyncWords *sync = nullptr;
+  WidthScratch wid[DSL_MAX_ROWS + 1];
+};
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(call)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess) return fail(DSL_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+static bool mult(int v, int m) { return v > 0 && v % m == 0; }
+
+static int validate_dims(const dsl_dims *d) {
+  if (d->max_rows < 1 || d->max_rows > DSL_MAX_ROWS)
+    return fail(DSL_EUNSUPPORTED, "max_rows %d outside 1..%d", d->max_rows, DSL_MAX_ROWS);
+  if (d->n_layers < 1 || d->n_layers > DSL_MAX_LAYERS)
+    return fail(DSL_EUNSUPPORTED, "n_layers %d outside 1..%d", d->n_layers, DSL_MAX_LAYERS);
+  if (!mult(d->hidden, 128)) return fail(DSL_EUNSUPPORTED, "hidden %d is not a positive multiple of 128", d->hidden);
+  if (!mult(d->q_rank, 128)) return fail(DSL_EUNSUPPORTED, "q_rank %d is not a positive multiple of 128", d->q_rank);
+  if (!mult(d->o_rank, 128)) return fail(DSL_EUNSUPPORTED, "o_rank %d is not a positive multiple of 128", d->o_rank);
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256 && d->head_dim != 512)
+    return fail(DSL_EUNSUPPORTED, "head_dim %d not in {64, 128, 256, 512}", d->head_dim);
+  if (d->n_heads < 1 || !mult(d->n_heads * d->head_dim, 128))
+    return fail(DSL_EUNSUPPORTED, "n_heads*head_dim %d is not a positive multiple of 128", d->n_heads * d->head_dim);
+  if (!mult(d->inter, 128)) return fail(DSL_EUNSUPPORTED, "inter %d is not a positive multiple of 128", d->inter);
+  if (!mult(d->shared_inter, 128))
+    return fail(DSL_EUNSUPPORTED, "shared_inter %d is not a positive multiple of 128", d->shared_inter);
+  if (d->n_experts < 1 || d->n_experts > 128)
+    return fail(DSL_EUNSUPPORTED, "n_experts %d outside 1..128", d->n_experts);
+  if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts)
+    return fail(DSL_EUNSUPPORTED, "top_k %d outside 1..min(8, n_experts)", d->top_k);
+  if (d->window < 1) return fail(DSL_EINVAL, "window %d < 1", d->window);
+  if (d->swa_width < 0) return fail(DSL_EINVAL, "swa_width %d < 0", d->swa_width);
+  if (d->kv_block < 1) return fail(DSL_EINVAL, "kv_block %d < 1", d->kv_block);
+  if (!(d->norm_eps >= 0.f) || !(d->swiglu_limit > 0.f))
+    return fail(DSL_EINVAL, "norm_eps must be >= 0 and swiglu_limit > 0");
+  return 0;
+}
+
+static int pick_kc(int K, int target) {
+  int kc = K < target ? K : target;
+  kc -= kc % 128;
+  while (kc > 128 && K % kc) kc -= 128;
+  return kc;
+}
+
+static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
+  const dsl_dims &d = L->d;
+  const Plan &pl = L->plan;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char * {
+    off = (off + 255) & ~(size_t)255;
+    char *p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  const size_t h = d.hidden, qr = d.q_rank, D = d.head_dim, HD = (size_t)d.n_heads * d.head_dim, orr = d.o_rank;
+  const size_t E = d.n_experts, k = d.top_k, I = d.inter, Is = d.shared_inter, S = L->S, m = M;
+  s->xb = (uint16_t *)take(m * h * 2);
+  s->p_qkv = (float *)take((h / pl.kc_qkv) * m * (qr + D) * 4);
+  s->qb = (uint16_t *)take(m * qr * 2);
+  s->p_q = (float *)take((qr / pl.kc_qb) * m * HD * 4);
+  s->att_o = (float *)take(m * d.n_heads * S * D * 4);
+  s->att_ml = (float *)take(m * d.n_heads * S * 2 * 4);
+  s->ob = (uint16_t *)take(m * HD * 2);
+  s->p_t = (float *)take((HD / pl.kc_oa) * m * orr * 4);
+  s->tb = (uint16_t *)take(m * orr * 2);
+  s->p_a = (float *)take((orr / pl.kc_ob) * m * h * 4);
+  s->xin = (uint16_t *)take(m * h * 2);
+  s->hres = (uint16_t *)take(m * h * 2);
+  s->u = (uint16_t *)take(m * h * 2);
+  s->logits = (float *)take(m * E * 4);
+  s->p_sh = (float *)take((h / pl.kc_sh13) * m * 2 * Is * 4);
+  s->zsh = (uint16_t *)take(m * Is * 2);
+  s->zr = (uint16_t *)take(m * k * I * 2);
+  s->y = (float *)take(m * k * h * 4);
+  s->p_shd = (float *)take((Is / pl.kc_shd) * m * h * 4);
+  return (off + 255) & ~(size_t)255;
+}
+
+static int get_width(dsl_layer *L, int M, Scratch *out) {
+  WidthScratch &w = L->wid[M];
+  if (!w.buf) {
+    Scratch tmp;
+    const size_t bytes = layout(L, M, &tmp, nullptr);
+    HIPCHK(hipSetDevice(L->dev));
+    if (hipMalloc(&w.buf, bytes) != hipSuccess) {
+      w.buf = nullptr;
+      return fail(DSL_ENOMEM, "scratch of width %d (%zu bytes) could not be allocated", M, bytes);
+    }
+    HIPCHK(hipMemset(w.buf, 0, bytes));
+    w.bytes = bytes;
+    layout(L, M, &w.s, (char *)w.buf);
+  }
+  *out = w.s;
+  return 0;
+}
+
+static int check_ptr16(const void *p, const char *what) {
+  if (!p) return fail(DSL_EINVAL, "%s is NULL", what);
+  if ((uintptr_t)p & 15) return fail(DSL_EINVAL, "%s is not 16-byte aligned", what);
+  return 0;
+}
+
+extern "C" {
+
+const char *dsl_last_error(void) { return g_err.c_str(); }
+
+int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer **out) {
+  if (!dims || !weights || !out) return fail(DSL_EINVAL, "dims, weights and out must be non-NULL");
+  *out = nullptr;
+  int rc = validate_dims(dims);
+  if (rc) return rc;
+  for (int l = 0; l < dims->n_layers; l++) {
+    const dsl_weights &w = weights[l];
+    const void *ptrs[] = {w.attn_norm, w.q_norm, w.kv_norm, w.ffn_norm, w.wqkv, w.wqkv_s, w.wq_b, w.wq_b_s,
+                          w.wo_a, w.wo_a_s, w.wo_b, w.wo_b_s, w.w_router, w.sh_w13, w.sh_w13_s, w.sh_wd,
+                          w.sh_wd_s, w.ex_w13, w.ex_w13_s, w.ex_wd, w.ex_wd_s};
+    for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; i++)
+      if ((rc = check_ptr16(ptrs[i], "a weight pointer"))) return fail(rc, "layer %d weight %zu: %s", l, i, g_err.c_str());
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DSL_EHIP, "no HIP device");
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, dev));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(DSL_EUNSUPPORTED, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
+  int coop = 0;
+  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  if (!coop) return fail(DSL_EUNSUPPORTED, "device %d does not support cooperative launches", dev);
+  int bpc = 0;
+  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel, kThreads, 0));
+  if (bpc < 1) return fail(DSL_EUNSUPPORTED, "the layer kernel cannot be resident on a compute unit");
+  if (bpc > 2) bpc = 2;
+  dsl_layer *L = new dsl_layer();
+  L->d = *dims;
+  L->dev = dev;
+  L->cus = prop.multiProcessorCount;
+  L->bpc = bpc;
+  L->grid = L->cus * bpc;
+  const int keys = dims->swa_width > 0 ? dims->swa_width : dims->window;
+  L->S = (keys + kSplitKeys - 1) / kSplitKeys;
+  L->plan.kc_qkv = pick_kc(dims->hidden, 512);
+  L->plan.kc_qb = pick_kc(dims->q_rank, 512);
+  L->plan.kc_oa = pick_kc(dims->n_heads * dims->head_dim, 512);
+  L->plan.kc_ob = pick_kc(dims->o_rank, 512);
+  L->plan.kc_sh13 = pick_kc(dims->hidden, 1024);
+  L->plan.kc_shd = pick_kc(dims->shared_inter, 512);
+  if (hipMalloc((void **)&L->sync, sizeof(SyncWords)) != hipSuccess ||
+      hipMalloc((void **)&L->dw, sizeof(dsl_weights) * dims->n_layers) != hipSuccess) {
+    dsl_layer_destroy(L);
+    return fail(DSL_ENOMEM, "sync buffer allocation failed");
+  }
+  if (hipMemset(L->sync, 0, sizeof(SyncWords)) != hipSuccess ||
+      hipMemcpy(L->dw, weights, sizeof(dsl_weights) * dims->n_layers, hipMemcpyHostToDevice) != hipSuccess) {
+    dsl_layer_destroy(L);
+    return fail(DSL_EHIP, "initializing the sync buffer failed");
+  }
+  *out = L;
+  return 0;
+}
+
+int dsl_layer_reserve(dsl_layer *L, int32_t M) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  if (M < 1 || M > L->d.max_rows) return fail(DSL_EUNSUPPORTED, "width %d outside 1..%d", M, L->d.max_rows);
+  Scratch s;
+  return get_width(L, M, &s);
+}
+
+static int check_kv(const dsl_layer *L, const dsl_kv *kv, int n) {
+  const dsl_dims &d = L->d;
+  const int64_t record = d.head_dim + 16;
+  for (int l = 0; l < n; l++) {
+    const dsl_kv &c = kv[l];
+    if (!c.base || !c.block_table || !c.row_req) return fail(DSL_EINVAL, "kv[%d]: base, block_table and row_req must be set", l);
+    if ((uintptr_t)c.base & 15) return fail(DSL_EINVAL, "kv[%d]: base is not 16-byte aligned", l);
+    if (c.block_stride < (int64_t)d.kv_block * record)
+      return fail(DSL_EINVAL, "kv[%d]: block stride %lld is below block * RECORD = %lld", l, (long long)c.block_stride,
+                  (long long)(d.kv_block * record));
+    if (c.block_stride % 16) return fail(DSL_EINVAL, "kv[%d]: block stride %lld is not a multiple of 16", l, (long long)c.block_stride);
+    if (c.n_blocks < 1 || c.max_blocks < 1 || c.n_req < 1)
+      return fail(DSL_EINVAL, "kv[%d]: n_blocks, max_blocks and n_req must be positive", l);
+    if (d.swa_width > 0 && !c.key_table) return fail(DSL_EINVAL, "kv[%d]: index-table mode needs key_table", l);
+  }
+  return 0;
+}
+
+static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv, const int32_t *pos, void *out,
+                  const dsl_taps *taps, void *stream) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  int rc;
+  if ((rc = check_ptr16(x, "input"))) return rc;
+  if ((rc = check_ptr16(out, "output"))) return rc;
+  if (M < 1 || M > L->d.max_rows) return fail(DSL_EUNSUPPORTED, "width %d outside 1..%d", M, L->d.max_rows);
+  const int nl = mode == kModeDecode ? L->d.n_layers : 1;
+  if (mode != kModeMoe) {
+    if (!kv || !pos) return fail(DSL_EINVAL, "kv and positions must be set");
+    if ((rc = check_kv(L, kv, nl))) return rc;
+  }
+  Params p{};
+  if ((rc = get_width(L, M, &p.s))) return rc;
+  const dsl_dims &d = L->d;
+  p.h = d.hidden; p.H = d.n_heads; p.D = d.head_dim; p.qr = d.q_rank; p.orr = d.o_rank;
+  p.W = d.window; p.swa = d.swa_width; p.E = d.n_experts; p.k = d.top_k; p.I = d.inter;
+  p.Is = d.shared_inter; p.B = d.kv_block; p.n_layers = nl;
+  p.eps = d.norm_eps; p.lim = d.swiglu_limit;
+  p.attn_scale = 1.0f / sqrtf((float)d.head_dim);
+  p.M = M; p.mode = mode; p.S = L->S; p.pl = L->plan;
+  p.w = L->dw;
+  if (kv)
+    for (int l = 0; l < nl; l++) p.kv[l] = kv[l];
+  p.pos = pos;
+  p.x = (const uint16_t *)x;
+  p.out = (uint16_t *)out;
+  if (taps) p.taps = *taps;
+  p.sync = L->sync;
+  void *args[] = {&p};
+  HIPCHK(hipSetDevice(L->dev));
+  HIPCHK(hipLaunchCooperativeKernel((const void *)dsl_layer_kernel, dim3(L->grid), dim3(kThreads), args, 0,
+                                    (hipStream_t)stream));
+  return 0;
+}
+
+int dsl_decode_step(dsl_layer *L, const void *x, int32_t M, const dsl_kv *kv, const int32_t *pos, void *out,
+                    const dsl_taps *taps, void *stream) {
+  return launch(L, kModeDecode, x, M, kv, pos, out, taps, stream);
+}
+
+int dsl_attn_step(dsl_layer *L, const void *x, int32_t M, const dsl_kv *kv, const int32_t *pos, void *out,
+                  void *stream) {
+  return launch(L, kModeAttn, x, M, kv, pos, out, nullptr, stream);
+}
+
+int dsl_moe_step(dsl_layer *L, const void *u, int32_t M, void *out, int32_t *ids, float *w, void *stream) {
+  dsl_taps t{};
+  t.topk_ids = ids;
+  t.topk_w = w;
+  return launch(L, kModeMoe, u, M, nullptr, nullptr, out, &t, stream);
+}
+
+int dsl_layer_health(dsl_layer *L) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  unsigned hw = 0;
+  HIPCHK(hipSetDevice(L->dev));
+  HIPCHK(hipMemcpy(&hw, &L->sync->health, sizeof hw, hipMemcpyDeviceToHost));
+  if (hw) {
+    HIPCHK(hipMemset(L->sync, 0, sizeof(SyncWords)));
+    return fail(DSL_EDEVICE, "device fault word 0x%x (%s%s)", hw, hw & kFaultBarrier ? "grid barrier timeout " : "",
+                hw & kFaultSlot ? "KV slot outside the cache" : "");
+  }
+  return 0;
+}
+
+int dsl_layer_grid(const dsl_layer *L, int32_t *blocks, int32_t *threads) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  if (blocks) *blocks = L->grid;
+  if (threads) *threads = kThreads;
+  return 0;
+}
+
+void dsl_layer_destroy(dsl_layer *L) {
+  if (!L) return;
+  for (auto &w : L->wid)
+    if (w.buf) (void)hipFree(w.buf);
+  if (L->sync) (void)hipFree(L->sync);
+  if (L->dw) (void)hipFree(L->dw);
+  delete L;
+}
+
+}  // extern "C"

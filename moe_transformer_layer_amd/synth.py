@@ -96,8 +96,8 @@ def _e8m0_for(rms: float, elem_rms: float, shape, rng) -> np.ndarray:
     """E8M0 bytes whose power of two brings codes of rms `elem_rms` to about `rms`,
     jittered by -1/0/+1 per block so blocks carry distinct, nonzero scales."""
     base = 127 + int(round(np.log2(rms / elem_rms)))
-    j = rng.integers(-1, 2, size=shape)
-    return (base + j).astype(np.uint8)
+    j = rng.integers(-1, 2, size=shape, dtype=np.int8)
+    return (j + np.int8(base - 128)).astype(np.uint8) + np.uint8(128)
 
 
 def _uniform_rms(a: float) -> float:
@@ -113,7 +113,7 @@ def gen_mxfp8_weight(n: int, k: int, amp: float, rng) -> tuple[np.ndarray, np.nd
     Values are about U(+-amp): codes from U(+-448), tile scales near amp/448."""
     codes = _e4m3_codes(rng.uniform(-E4M3_MAX_DRAW, E4M3_MAX_DRAW, size=(n, k)).astype(np.float32))
     base = 127 + int(round(np.log2(amp / E4M3_MAX_DRAW)))
-    scales = (base + rng.integers(-1, 2, size=(n // 32, k // 32))).astype(np.uint8)
+    scales = (base + rng.integers(-1, 2, size=(n // 32, k // 32), dtype=np.int8)).astype(np.uint8)
     return codes, scales
 
 
@@ -127,7 +127,7 @@ def gen_fp8_block_weight(n: int, k: int, amp: float, rng) -> tuple[np.ndarray, n
 def gen_mxfp4_experts(e: int, n: int, k: int, amp: float, rng) -> tuple[np.ndarray, np.ndarray]:
     """e2m1 nibbles [e, n, k/2] (low nibble = even k) with one E8M0 per 32 along k
     [e, n, k/32].  Nibbles are uniform over all 16 codes."""
-    packed = np.frombuffer(rng.bytes(e * n * (k // 2)), dtype=np.uint8).reshape(e, n, k // 2).copy()
+    packed = rng.integers(0, 256, size=(e, n, k // 2), dtype=np.uint8)
     scales = _e8m0_for(_uniform_rms(amp), _E2M1_CODE_RMS, (e, n, k // 32), rng)
     return packed, scales
 
@@ -252,24 +252,37 @@ class Case:
     seed: int
 
 
-def make_case(name: str, seed: int, M: int | None = None, n_pad: int = 0,
-              n_req: int | None = None, rows_per_req: int | None = None,
-              n_layers: int | None = None, ctx: tuple | None = None,
-              gate_gain: float = 1.0) -> Case:
-    """Draw one workload.  name picks the dims; M, n_req, rows_per_req override the row
-    layout (rows = n_req * rows_per_req + n_pad)."""
+def make_weights(name: str, weights_seed: int, n_layers: int | None = None, gate_gain: float = 1.0) -> list:
+    """The layers' weights of workload `name`, drawn from their own seed."""
     d = CONFIGS[name]
     if n_layers is not None:
         d = d.replace(n_layers=n_layers)
-    rng = np.random.default_rng(seed)
-    layers = [gen_layer_weights(d, rng, attn_amp=0.05 if name == "tiny" else None, gate_gain=gate_gain)
-              for _ in range(d.n_layers)]
+    rng = np.random.default_rng([weights_seed, 0])
+    return [gen_layer_weights(d, rng, attn_amp=0.05 if name == "tiny" else None, gate_gain=gate_gain)
+            for _ in range(d.n_layers)]
+
+
+def make_case(name: str, seed: int, M: int | None = None, n_pad: int = 0,
+              n_req: int | None = None, rows_per_req: int | None = None,
+              n_layers: int | None = None, ctx: tuple | None = None,
+              gate_gain: float = 1.0, weights_seed: int | None = None,
+              layers: list | None = None) -> Case:
+    """Draw one workload.  name picks the dims; M, n_req, rows_per_req override the row
+    layout (rows = n_req * rows_per_req + n_pad).  Weights come from weights_seed
+    (default: seed) unless `layers` passes weights already drawn; activations, caches
+    and tables come from seed."""
+    d = CONFIGS[name]
+    if n_layers is not None:
+        d = d.replace(n_layers=n_layers)
+    if layers is None:
+        layers = make_weights(name, seed if weights_seed is None else weights_seed, n_layers, gate_gain)
+    assert len(layers) == d.n_layers
+    rng = np.random.default_rng([seed, 1])
     if name == "moe6":
         M = M or 6
         x = gen_x(d, rng, M, truncate=None)
         return Case(d, layers, None, x, M, seed)
     if name == "tiny":
-        n_req, rows_per_req = 1, 1
         kv = gen_kv(d, rng, 1, 1, 16, 63, fill_all=True)
         x = gen_x(d, rng, 1, truncate=None)
         return Case(d, layers, kv, x, 1, seed)

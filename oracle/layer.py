@@ -36,8 +36,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import (bf16_encode, bf16_round, bf16_value, dequant_fp8_block128,
-                      dequant_mxfp4, dequant_mxfp8_weight, e4m3_encode, e4m3_value, f32,
+from .cgemv import gemv_fp8b128, gemv_mxfp4, gemv_mxfp8
+from .formats import (bf16_encode, bf16_round, bf16_value, e4m3_encode, e4m3_value, f32,
                       mx_e4m3_dequant_act, mx_e4m3_quantize)
 
 
@@ -56,7 +56,7 @@ def mxfp8_linear(x: np.ndarray, w: np.ndarray, ws: np.ndarray) -> np.ndarray:
     quantized per 1x32 block along K straight from float32 (R2); the result is float32
     (R3)."""
     xq, xs = mx_e4m3_quantize(x)
-    return f32(mx_e4m3_dequant_act(xq, xs) @ dequant_mxfp8_weight(w, ws).T)
+    return f32(gemv_mxfp8(w, ws, mx_e4m3_dequant_act(xq, xs)))
 
 
 def kv_record(kv: np.ndarray, head_dim: int) -> np.ndarray:
@@ -209,31 +209,30 @@ def moe_half(d, lw: dict, u_bits: np.ndarray, live: np.ndarray | None = None) ->
     ids, w = router_topk(logits, d.top_k)
     ids[~live] = -1
     w[~live] = 0.0
-    sh13 = dequant_fp8_block128(lw["sh_w13"], lw["sh_w13_s"])
-    shd = dequant_fp8_block128(lw["sh_wd"], lw["sh_wd_s"])
-    gu = f32(u @ sh13.T)
+    gu = f32(gemv_fp8b128(lw["sh_w13"], lw["sh_w13_s"], u))
     z_sh = bf16_round(swiglu_clamp(gu[:, :Is], gu[:, Is:], d.swiglu_limit))
-    ys = f32(z_sh @ shd.T)
+    ys = f32(gemv_fp8b128(lw["sh_wd"], lw["sh_wd_s"], z_sh))
     y = np.zeros((M, d.top_k, d.hidden))
-    cache13, cached = {}, {}
+    # each selected expert once, on all (row, slot) pairs that chose it
+    pairs = {}
     for m in range(M):
-        if not live[m]:
-            continue
-        for j in range(d.top_k):
-            e = int(ids[m, j])
-            if e not in cache13:
-                cache13[e] = dequant_mxfp4(lw["ex_w13"][e], lw["ex_w13_s"][e])
-                cached[e] = dequant_mxfp4(lw["ex_wd"][e], lw["ex_wd_s"][e])
-            gu_e = f32(cache13[e] @ u[m])
-            z = bf16_round(swiglu_clamp(gu_e[:I], gu_e[I:], d.swiglu_limit))
-            y[m, j] = f32(cached[e] @ z)
+        if live[m]:
+            for j in range(d.top_k):
+                pairs.setdefault(int(ids[m, j]), []).append((m, j))
+    for e, pl in sorted(pairs.items()):
+        rows = [m for m, _ in pl]
+        gu_e = f32(gemv_mxfp4(lw["ex_w13"][e], lw["ex_w13_s"][e], u[rows]))
+        z = bf16_round(swiglu_clamp(gu_e[:, :I], gu_e[:, I:], d.swiglu_limit))
+        ye = f32(gemv_mxfp4(lw["ex_wd"][e], lw["ex_wd_s"][e], z))
+        for (m, j), yy in zip(pl, ye):
+            y[m, j] = yy
     mo = ys.copy()
     for j in range(d.top_k):
         mo = mo + w[:, j:j + 1] * y[:, j]
     mo = f32(mo)
     mo[~live] = 0.0
-    return dict(m=mo, ids=ids, w=w, logits=logits, ys=ys, y=y, z_sh=z_sh,
-                n_distinct=len(cache13))
+    return dict(m=mo, ids=ids, w=w, logits=logits, ys=ys, y=y, z_sh=z_sh, gu_sh=gu,
+                n_distinct=len(pairs))
 
 
 # ----------------------------------------------------------------------------- entry points

@@ -1,0 +1,95 @@
+"""The C ABI library loads, exports every symbol include/dsl.h declares, and refuses bad
+arguments on the host before touching a device.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_transformer_layer_amd import dsl, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dsl.h")).read()
+    return sorted(set(re.findall(r"\b(dsl_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsl.LIB_PATH):
+        pytest.skip("libdsl.so not built")
+    return dsl.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert "dsl_layer_build" in names and "dsl_decode_step" in names and "dsl_moe_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_structs_match_binding():
+    src = open(os.path.join(ROOT, "include", "dsl.h")).read()
+    body = src[src.index("typedef struct {\n  const float *attn_norm"):]
+    body = body[: body.index("} dsl_weights;")]
+    names = re.findall(r"\*\s*([a-z0-9_]+)", body)
+    assert tuple(names) == dsl.WEIGHT_FIELDS
+    assert ctypes.sizeof(dsl.Dims) == 16 * 4
+    assert ctypes.sizeof(dsl.KV) == 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
+
+
+def _weights_stub():
+    # 16-byte aligned non-null fake pointers: never dereferenced by a refused build
+    return dsl.Weights(**{n: 0x1000 * (i + 1) for i, n in enumerate(dsl.WEIGHT_FIELDS)})
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(max_rows=49), dsl.DSL_EUNSUPPORTED),
+    (dict(max_rows=0), dsl.DSL_EUNSUPPORTED),
+    (dict(hidden=4000), dsl.DSL_EUNSUPPORTED),
+    (dict(head_dim=96), dsl.DSL_EUNSUPPORTED),
+    (dict(n_experts=129), dsl.DSL_EUNSUPPORTED),
+    (dict(top_k=9), dsl.DSL_EUNSUPPORTED),
+    (dict(inter=100), dsl.DSL_EUNSUPPORTED),
+    (dict(n_layers=5), dsl.DSL_EUNSUPPORTED),
+    (dict(window=0), dsl.DSL_EINVAL),
+    (dict(kv_block=0), dsl.DSL_EINVAL),
+])
+def test_build_refuses_bad_dims(lib, change, code):
+    d = synth.CONFIGS["layer48"].replace(**change)
+    h = ctypes.c_void_p()
+    rc = lib.dsl_layer_build(ctypes.byref(dsl.dims_struct(d)), ctypes.byref(_weights_stub()), ctypes.byref(h))
+    assert rc == code, dsl.dsl_last_error()
+    assert not h.value
+    assert dsl.dsl_last_error()
+
+
+def test_build_refuses_null_and_misaligned(lib):
+    d = dsl.dims_struct(synth.CONFIGS["tiny"])
+    h = ctypes.c_void_p()
+    assert lib.dsl_layer_build(None, ctypes.byref(_weights_stub()), ctypes.byref(h)) == dsl.DSL_EINVAL
+    w = _weights_stub()
+    w.wq_b = 0x1008
+    assert lib.dsl_layer_build(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h)) == dsl.DSL_EINVAL
+    assert "aligned" in dsl.dsl_last_error()
+    w = _weights_stub()
+    w.ex_wd_s = None
+    assert lib.dsl_layer_build(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h)) == dsl.DSL_EINVAL
+
+
+def test_steps_refuse_null_handle(lib):
+    assert lib.dsl_decode_step(None, None, 1, None, None, None, None, None) == dsl.DSL_EINVAL
+    assert lib.dsl_moe_step(None, None, 1, None, None, None, None) == dsl.DSL_EINVAL
+    assert lib.dsl_attn_step(None, None, 1, None, None, None, None) == dsl.DSL_EINVAL
+    assert lib.dsl_layer_reserve(None, 6) == dsl.DSL_EINVAL
+    assert lib.dsl_layer_health(None) == dsl.DSL_EINVAL
+    lib.dsl_layer_destroy(None)
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dsl, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(dsl, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        dsl.lib()

@@ -1,0 +1,131 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded
+inputs, element by element.  Small multi-tile shapes with ragged row counts and pad
+rows first, then every workload at its full size in the launch configuration the
+bench times."""
+import numpy as np
+import pytest
+
+from moe_transformer_layer_amd import synth
+from oracle import layer as OL
+from parity import (check_bf16, check_records, check_routing, decode_live, gap_seed, min_gap,
+                    oracle_decode, GAP_MIN)
+
+pytestmark = pytest.mark.gpu
+
+W_TOL_MOE = 1e-5     # MoE-only steps: both sides read the same bf16 input
+W_TOL_LAYER = 1e-4   # full steps: the MoE input may differ by one bf16 rounding flip per element
+
+
+@pytest.fixture(scope="module")
+def dsl(gpu):
+    from moe_transformer_layer_amd import dsl as d
+    d.lib()
+    return d
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def run_decode(dsl, case, res, want_caches, w_tol, report=None):
+    dev = dsl.LayerOnDevice(case)
+    try:
+        _say(f"decode dims={case.dims.hidden}/{case.dims.n_experts} layers={case.dims.n_layers} "
+             f"M={case.M} seed={case.seed}")
+        got = dev.decode(case.x)
+        got_caches = dev.caches_host()
+    finally:
+        dev.close()
+    rep = {} if report is None else report
+    live = decode_live(case)
+    for key in ("out", "attn_out", "hres", "moe_in", "moe_out"):
+        check_bf16(key, got[key], res[key], rep)
+    check_routing(got["ids"], got["w"], res["ids"], res["w"], live, w_tol, rep)
+    for l in range(case.dims.n_layers):
+        check_records(case.dims, got_caches[l], want_caches[l], case.kv.cache[l], rep)
+    _say(f"ok {rep}")
+    return rep
+
+
+def _decode_case(name, key, first=0, **kw):
+    def run(c):
+        res, caches = oracle_decode(c)
+        return (res, caches), res["layers"]
+
+    return gap_seed(name, key, lambda s: synth.make_case(name, s, **kw), run, decode_live, first=first)
+
+
+# ------------------------------------------------------------------ small shapes
+
+def test_tiny_layer_m1(dsl):
+    case, (res, caches) = _decode_case("tiny", "tiny")
+    run_decode(dsl, case, res, caches, W_TOL_LAYER)
+
+
+@pytest.mark.parametrize("n_req,rows,n_pad", [(2, 6, 1), (1, 5, 0), (3, 4, 0)])
+def test_mid_layer_ragged(dsl, n_req, rows, n_pad):
+    case, (res, caches) = _decode_case("mid", f"mid_{n_req}x{rows}+{n_pad}", first=100,
+                                       n_req=n_req, rows_per_req=rows, n_pad=n_pad)
+    run_decode(dsl, case, res, caches, W_TOL_LAYER)
+
+
+def test_mid_layer_clamp_active(dsl):
+    """Large gate/up weights drive the SwiGLU clamp on many elements."""
+    case, (res, caches) = _decode_case("mid", "mid_clamp", first=200, gate_gain=4.0)
+    assert (np.abs(res["moe"]["gu_sh"]) > case.dims.swiglu_limit).mean() > 0.01
+    run_decode(dsl, case, res, caches, W_TOL_LAYER)
+
+
+def test_mid_draft_two_layers(dsl):
+    case, (res, caches) = _decode_case("mid_draft", "mid_draft", first=300, n_pad=1)
+    run_decode(dsl, case, res, caches, W_TOL_LAYER)
+
+
+def test_mid_attention_only(dsl):
+    case = synth.make_case("mid", 400, n_pad=1)
+    caches = [c.copy() for c in case.kv.cache]
+    want = OL.attn_step(case.dims, case.layers[0], case.x, case.kv, caches[0])
+    dev = dsl.LayerOnDevice(case)
+    try:
+        _say(f"attn mid M={case.M}")
+        got = dev.attn(case.x)
+        gc = dev.caches_host()
+    finally:
+        dev.close()
+    check_bf16("attn_out", got["attn_out"], want["attn_out"])
+    check_records(case.dims, gc[0], caches[0], case.kv.cache[0])
+
+
+def test_mid_moe_only(dsl):
+    d = synth.CONFIGS["mid"]
+
+    def make(s):
+        c = synth.make_case("mid", s)
+        return c
+
+    def run(c):
+        r = OL.moe_step(d, c.layers[0], c.x)
+        return r, [r]
+
+    case, res = gap_seed("mid", "mid_moe", make, run, lambda c: np.ones(c.M, bool), first=500)
+    dev = dsl.LayerOnDevice(case)
+    try:
+        _say(f"moe mid M={case.M}")
+        got = dev.moe(case.x)
+    finally:
+        dev.close()
+    check_bf16("moe_out", got["moe_out"], res["moe_out"])
+    check_routing(got["ids"], got["w"], res["ids"], res["w"], np.ones(case.M, bool), W_TOL_MOE)
+
+
+def test_repeat_launch_bit_exact(dsl):
+    """Two launches of the same step give bit-identical outputs (no value atomics)."""
+    case = synth.make_case("mid", 600)
+    dev = dsl.LayerOnDevice(case)
+    try:
+        a = dev.decode(case.x)
+        b = dev.decode(case.x)
+    finally:
+        dev.close()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
