@@ -1,0 +1,208 @@
+"""Benchmark of the decode layer on one MI355X.
+
+A step is one decode layer (the whole hot path: attention front, split attention,
+attention back, MoE) over one batch of rows, launched through the C ABI as one
+persistent kernel.  Weights are cold: the bench holds L distinct copies of the
+layer's weights in HBM (as a model holds distinct layers) and step i runs copy
+i mod L, so no step finds the previous one's weights in the 256 MB Infinity Cache.
+
+Prints one JSON line: the M=6 full layer (top-6 of 128 experts) as the headline,
+the M=48 layer as a second point, the roofline of the launch (algorithmic HBM
+bytes per step over the measured kernel time against 8 TB/s), and the CPU oracle
+timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def algorithmic_bytes(d, M: int, ids, kv) -> dict:
+    """Bytes the step must move: every weight read once (each distinct selected expert
+    once), the KV records read (union of the rows' windows per request) and written,
+    and the activations in and out."""
+    h, qr, D, HD, orr = d.hidden, d.q_rank, d.head_dim, d.n_heads * d.head_dim, d.o_rank
+    E, I, Is = d.n_experts, d.inter, d.shared_inter
+
+    def mx8(n, k):
+        return n * k + (n // 32) * (k // 32)
+
+    attn = mx8(qr + D, h) + mx8(HD, qr) + mx8(orr, HD) + mx8(h, orr) + 4 * (2 * h + qr + D)
+    router = 4 * E * h
+    shared = 3 * h * Is + 4 * ((2 * Is // 128) * (h // 128) + (h // 128) * (Is // 128))
+    per_expert = 3 * h * I // 2 + 3 * h * I // 32
+    live = [i for i in range(M) if kv.positions[i] >= 0]
+    distinct = sorted({int(e) for i in live for e in ids[i]})
+    rec = D + 16
+    seen = set()
+    for i in live:
+        p, q = int(kv.positions[i]), int(kv.row_req[i])
+        for t in range(max(0, p - d.window + 1), p + 1):
+            seen.add((q, t))
+    kv_read = len(seen) * rec
+    kv_write = len(live) * rec
+    act = 2 * M * h * 2
+    total = attn + router + shared + len(distinct) * per_expert + kv_read + kv_write + act
+    return dict(total=total, attention=attn, router=router, shared=shared, experts=len(distinct) * per_expert,
+                n_distinct=len(distinct), kv=kv_read + kv_write, act=act)
+
+
+def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup: int, weights, seed: int = 0):
+    from moe_transformer_layer_amd import synth
+    case = synth.make_case(name, seed, M=M, layers=weights)
+    d = case.dims
+    dev = dsl.LayerOnDevice(case)
+    # distinct weight copies for cold-weight steps
+    handles = [dev.handle]
+    copies = []
+    for _ in range(layers_dev - 1):
+        wd = {k: v.clone() for k, v in dev.w_dev[0].items()}
+        copies.append(wd)
+        ws = dsl.Weights(**{k: wd[k].data_ptr() for k in dsl.WEIGHT_FIELDS})
+        handles.append(dsl.dsl_layer_build(dsl.dims_struct(d), [ws]))
+    x = torch.from_numpy(case.x.view("int16")).to(dev.dev)
+    out = torch.zeros_like(x)
+    ids = torch.zeros((M, d.top_k), dtype=torch.int32, device=dev.dev)
+    taps = dsl.Taps(None, None, None, None, ids.data_ptr(), None, None, None)
+    stream = dev.stream()
+    for hnd in handles:
+        dsl.dsl_layer_reserve(hnd, M)
+    dsl.dsl_decode_step(handles[0], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(), out.data_ptr(),
+                        taps, stream)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+
+    def step(i):
+        dsl.dsl_decode_step(handles[i % len(handles)], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(),
+                            out.data_ptr(), None, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for hnd in handles:
+        rc = dsl.dsl_layer_health(hnd)
+        if rc:
+            raise RuntimeError(f"device fault reported: {dsl.dsl_last_error()}")
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # microseconds per launch
+    mean_us = sum(per) / len(per)
+    byts = algorithmic_bytes(d, M, ids_h, case.kv)
+    gbs = byts["total"] / (mean_us * 1e-6) / 1e9
+    for hnd in handles[1:]:
+        dsl.dsl_layer_destroy(hnd)
+    grid = dsl.dsl_layer_grid(dev.handle)
+    dev.close()
+    del copies
+    torch.cuda.empty_cache()
+    return dict(M=M, us_per_layer_wall=wall / steps * 1e6, us_kernel_mean=mean_us, us_kernel_p10=per[len(per) // 10],
+                us_kernel_p50=per[len(per) // 2], us_kernel_p90=per[(9 * len(per)) // 10], gbs=gbs,
+                frac=gbs / PEAK_GBS, bytes=byts, grid=grid, n_weight_copies=len(handles))
+
+
+def cpu_baseline(name: str, M: int, weights, seconds: float = 12.0) -> dict:
+    """The oracle (one thread) on the same workload: whole decode steps until about
+    `seconds` of CPU work have run."""
+    from threadpoolctl import threadpool_limits
+
+    from moe_transformer_layer_amd import synth
+    from oracle import layer as OL
+    case = synth.make_case(name, 0, M=M, layers=weights)
+    n, t_all = 0, 0.0
+    with threadpool_limits(1):
+        while t_all < seconds and n < 20:
+            caches = [c.copy() for c in case.kv.cache]
+            t = time.perf_counter()
+            OL.decode_step(case.dims, case.layers, case.x, case.kv, caches)
+            t_all += time.perf_counter() - t
+            n += 1
+    return dict(value=t_all / n * 1e6, unit="us/decode layer", cores=1, kind="oracle",
+                sample=f"{n} whole decode steps of the M={M} full layer (hidden 4096, top-6 of 128), "
+                       f"{t_all:.1f} s of single-threaded CPU time", cpu=_cpu_model(), host_cores=os.cpu_count())
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="distinct weight copies rotated for cold weights")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--only-m6", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU only (asked for {args.gpus}): this library has no multi-GPU path; "
+              "tensor-parallel sharding is a design note, not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from moe_transformer_layer_amd import dsl, synth
+    dsl.lib()
+    assert torch.cuda.is_available(), "no GPU"
+    print("[bench] drawing the layer's weights", flush=True)
+    weights = synth.make_weights("layer48", 7)
+    print(f"[bench] M=6 full layer, {args.copies} weight copies, {args.steps} steps", flush=True)
+    m6 = run_point(dsl, torch, "layer48", 6, args.copies, args.steps, args.warmup, weights)
+    print(f"[bench] M=6: {m6['us_kernel_mean']:.1f} us/launch, {m6['gbs']:.0f} GB/s", flush=True)
+    m48 = None
+    if not args.only_m6:
+        print("[bench] M=48 full layer", flush=True)
+        m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights)
+        print(f"[bench] M=48: {m48['us_kernel_mean']:.1f} us/launch, {m48['gbs']:.0f} GB/s", flush=True)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] oracle cpu baseline", flush=True)
+        cpu = cpu_baseline("layer48", 6, weights)
+    line = {
+        "metric": "us/decode layer and HBM GB/s (% of peak) at M=6 and M=48 rows",
+        "value": round(m6["us_per_layer_wall"], 2),
+        "unit": "us/decode layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m6["us_per_layer_wall"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "full decode layer, M=6 rows (1 request x (1+5 drafts)), hidden 4096, 16 heads x 512, "
+                               "q/o rank 1024, window 128, top-6 of 128 MXFP4 experts (inter 2048), FP8 shared 2048, "
+                               "cold weights", "rows": 6, "seq_context": "1k-64k paged, block 128"},
+        "roofline": {"bound": "hbm", "achieved": round(m6["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(m6["frac"], 4), "traffic": None,
+                     "algorithmic_bytes": m6["bytes"]["total"], "kernel_us_mean": round(m6["us_kernel_mean"], 2)},
+        "m6": m6,
+        "m48": m48,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -135,6 +135,7 @@ typedef struct {
   int32_t *topk_ids;  /* [M][top_k], emitted in descending logit order           */
   float *topk_w;      /* [M][top_k]                                              */
   float *logits;      /* [M][n_experts] f32 router logits                        */
+  int32_t *layer_ids; /* [n_layers][M][top_k]: the expert ids of every layer     */
 } dsl_taps;
 
 typedef struct dsl_layer dsl_layer;
@@ -171,6 +172,14 @@ int dsl_moe_step(dsl_layer *layer, const void *u_bf16, int32_t M, void *moe_out_
  * synchronized.  0 = healthy; DSL_EDEVICE after a recorded device fault (the word
  * is then cleared and the handle's sync state reset). */
 int dsl_layer_health(dsl_layer *layer);
+
+/* Tracing for profiling: with on != 0, block 0 of every later launch stamps the
+ * device wall clock at the launch's start, after each grid barrier (one stamp per
+ * stage boundary) and at its end.  dsl_layer_read_trace copies the stamps of the
+ * most recent traced launch (call after synchronizing) as nanoseconds since its
+ * start into ns[0..n) and returns how many it wrote. */
+int dsl_layer_set_trace(dsl_layer *layer, int32_t on);
+int dsl_layer_read_trace(dsl_layer *layer, double *ns, int32_t n);
 
 /* Grid the persistent launch uses (blocks, threads per block); for reports. */
 int dsl_layer_grid(const dsl_layer *layer, int32_t *blocks, int32_t *threads);

@@ -112,47 +112,90 @@ __device__ __forceinline__ float group_max(float v) {
 
 // ------------------------------------------------------------------ loads / stores
 
-__device__ __forceinline__ v4u ld16(const void *p) { return *reinterpret_cast<const v4u *>(p); }
-__device__ __forceinline__ void st16(void *p, v4u v) { *reinterpret_cast<v4u *>(p) = v; }
+// Every buffer the kernel touches is device (global) memory.  Pointers reach the
+// kernel through structs, so the compiler cannot infer that and would emit FLAT
+// accesses, whose completion counts against the LDS/scalar counter too (every LDS
+// wait would then drain all outstanding loads).  These helpers address the global
+// segment explicitly.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *gptr(const T *p) {
+  return (const __attribute__((address_space(1))) T *)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *gptr(T *p) {
+  return (__attribute__((address_space(1))) T *)p;
+}
+template <class T>
+__device__ __forceinline__ T ldg(const T *p) { return *gptr(p); }
+template <class T>
+__device__ __forceinline__ void stg(T *p, T v) { *gptr(p) = v; }
+__device__ __forceinline__ v4u ld16(const void *p) { return ldg(reinterpret_cast<const v4u *>(p)); }
+__device__ __forceinline__ void st16(void *p, v4u v) { stg(reinterpret_cast<v4u *>(p), v); }
+__device__ __forceinline__ float4 ld_f4(const float *p) {
+  const v4f t = ldg(reinterpret_cast<const v4f *>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void st_f4(float *p, float4 v) { stg(reinterpret_cast<v4f *>(p), v4f{v.x, v.y, v.z, v.w}); }
+__device__ __forceinline__ float2 ld_f2(const float *p) {
+  const v2f t = ldg(reinterpret_cast<const v2f *>(p));
+  return make_float2(t[0], t[1]);
+}
+__device__ __forceinline__ void st_f2(float *p, float2 v) { stg(reinterpret_cast<v2f *>(p), v2f{v.x, v.y}); }
 
 // ------------------------------------------------------------------ grid barrier
 
-// Sync words of a handle (one 256-byte line each, in device memory).
+// Sync words of a handle (each counter on a 256-byte line of its own).
 struct SyncWords {
-  unsigned count;       // arrivals at the current barrier
-  unsigned pad0[63];
-  unsigned generation;  // completed barriers (monotonic; the barrier's epoch tag)
+  unsigned group[8][64];  // arrivals per group of blocks (block index mod 8)
+  unsigned top[64];       // groups fully arrived
+  unsigned generation;    // completed barriers (monotonic; the barrier's epoch tag)
   unsigned pad1[63];
-  unsigned health;      // 0, or a DSL device fault code
+  unsigned health;        // 0, or a DSL device fault code
   unsigned pad2[63];
-  unsigned tasks[64];   // task-queue counters (zeroed at each launch before use)
+  unsigned tasks[64];     // task-queue counters (zeroed at each launch before use)
 };
 
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 
 // All blocks of the launch meet here.  Writes before the barrier are visible to
 // every block after it (agent-scope release by each arriving block, acquire after).
-// The spin is bounded: a barrier that does not complete records kFaultBarrier in the
-// health word and lets the block go on, so the launch always drains.
+// Arrivals are counted in two levels (8 group counters, then one top counter) so no
+// single address takes more than nblocks/8 atomics.  The spin is bounded: a barrier
+// that does not complete records kFaultBarrier in the health word and lets the block
+// go on, so the launch always drains.
 __device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned gen = __hip_atomic_load(&sw->generation, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned arrived = __hip_atomic_fetch_add(&sw->count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == nblocks - 1) {
-      __hip_atomic_store(&sw->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&sw->generation, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+    const unsigned grp = blockIdx.x & 7u;
+    const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
+    const unsigned per = (nblocks - grp + 7u) / 8u;  // blocks in this group
+    const unsigned gen = __hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // release: this block's writes become visible before its arrival is counted
+    const unsigned a = __hip_atomic_fetch_add(gptr(&sw->group[grp][0]), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    bool released = false;
+    if (a == per - 1u) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(gptr(&sw->group[grp][0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned b = __hip_atomic_fetch_add(gptr(&sw->top[0]), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (b == ngroups - 1u) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(gptr(&sw->top[0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(gptr(&sw->generation), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        released = true;
+      }
+    }
+    if (!released) {
+      // poll without cache maintenance; one acquire once the generation moved
       unsigned spins = 0;
-      while (__hip_atomic_load(&sw->generation, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+      while (__hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > (1u << 24)) {
-          __hip_atomic_fetch_or(&sw->health, (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(gptr(&sw->health), (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }

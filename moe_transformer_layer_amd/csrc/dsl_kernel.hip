@@ -21,16 +21,30 @@ namespace dsl {
 
 // ============================================================== attention front
 
+// Row stages run one row per block: every thread holds E contiguous values, issues
+// all of its loads at once, and block reductions combine the rows' sums.
+
 // RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values)
-__device__ void st_attn_norm(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *xin) {
-  for (int m = cx.gw; m < p.M; m += cx.nw) {
-    const uint16_t *row = xin + (size_t)m * p.h;
-    auto load4 = [&](int k) {
-      const v2u v = *reinterpret_cast<const v2u *>(row + k);
-      return make_float4(bf16_to_f32(v[0] & 0xFFFFu), bf16_to_f32(v[0] >> 16), bf16_to_f32(v[1] & 0xFFFFu),
-                         bf16_to_f32(v[1] >> 16));
-    };
-    wave_row_mxq(load4, p.h, w.attn_norm, p.eps, p.s.xb + (size_t)m * p.h, cx.lane);
+template <int E>
+__device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, float *red) {
+  const int n = p.h, k = threadIdx.x * E;
+  const bool act = k < n;
+  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+    float v[E];
+    if (act)
+      load_bf16<E>(xin + (size_t)m * n + k, v);
+    else
+#pragma unroll
+      for (int e = 0; e < E; e++) v[e] = 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; e++) ss += v[e] * v[e];
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
+#pragma unroll
+    for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * ldg(w.attn_norm + k + e) : 0.f;
+    mx_quant_dequant<E>(v);
+    if (act) store_bf16<E>(p.s.xb + (size_t)m * n + k, v);
   }
 }
 
@@ -39,7 +53,7 @@ __device__ void st_attn_norm(const Params &p, const Ctx &cx, const dsl_weights &
 __device__ __forceinline__ uint8_t *record_ptr(const Params &p, const dsl_kv &kv, int64_t slot) {
   const int64_t blk = slot / p.B;
   if (slot < 0 || blk >= kv.n_blocks) {
-    __hip_atomic_fetch_or(&p.sync->health, (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(gptr(&p.sync->health), (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return nullptr;
   }
   return kv.base + blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
@@ -49,108 +63,127 @@ __device__ __forceinline__ uint8_t *record_ptr(const Params &p, const dsl_kv &kv
 __device__ __forceinline__ int64_t slot_of(const Params &p, const dsl_kv &kv, int req, int t) {
   const int lb = t / p.B;
   if (req < 0 || req >= kv.n_req || t < 0 || lb >= kv.max_blocks) return -1;
-  const int blk = kv.block_table[(size_t)req * kv.max_blocks + lb];
+  const int blk = ldg(kv.block_table + (size_t)req * kv.max_blocks + lb);
   return blk < 0 ? -1 : (int64_t)blk * p.B + (t - lb * p.B);
 }
 
-// q latent: sum the split-K partials, RMSNorm, MXFP8.  kv latent: RMSNorm, then the
-// fp8 record (codes e4m3(v / s), s = amax / 448) written at the row's slot.
-__device__ void st_qkv_post(const Params &p, const Ctx &cx, const dsl_weights &w, const dsl_kv &kv) {
-  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv;
-  const size_t pstride = (size_t)p.M * N;
-  for (int m = cx.gw; m < p.M; m += cx.nw) {
-    const float *base = p.s.p_qkv + (size_t)m * N;
-    auto load4 = [&](int k) {
-      float4 a = *reinterpret_cast<const float4 *>(base + k);
-      for (int ks = 1; ks < nks; ks++) {
-        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-      return a;
-    };
-    wave_row_mxq(load4, p.qr, w.q_norm, p.eps, p.s.qb + (size_t)m * p.qr, cx.lane);
-    const int pos = p.pos[m];
-    if (pos < 0) continue;  // pad row: no KV write
-    const int D = p.D;
-    float v[2][4];
-    float ss = 0.f;
+// q latent: sum the split-K partials, RMSNorm, MXFP8.
+template <int E>
+__device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red) {
+  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.qr, k = threadIdx.x * E;
+  const bool act = k < n;
+  float v[E];
+  if (act)
+    load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + k, (size_t)p.M * N, nks, v);
+  else
 #pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const int k = 4 * cx.lane + 256 * c;
-      if (k < D) {
-        const float4 a = load4(p.qr + k);
-        v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
-      } else {
-        v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
-      }
+    for (int e = 0; e < E; e++) v[e] = 0.f;
+  float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; e++) ss += v[c][e] * v[c][e];
+  for (int e = 0; e < E; e++) ss += v[e] * v[e];
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
+#pragma unroll
+  for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * ldg(w.q_norm + k + e) : 0.f;
+  mx_quant_dequant<E>(v);
+  if (act) store_bf16<E>(p.s.qb + (size_t)m * n + k, v);
+}
+
+// kv latent: RMSNorm, then the fp8 record (codes e4m3(v / s), s = amax / 448, then 12
+// zero bytes) at the row's slot.
+template <int E>
+__device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w, const dsl_kv &kv, int m, float *red) {
+  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = threadIdx.x * E;
+  const bool act = k < n;
+  float v[E];
+  if (act)
+    load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + p.qr + k, (size_t)p.M * N, nks, v);
+  else
+#pragma unroll
+    for (int e = 0; e < E; e++) v[e] = 0.f;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; e++) ss += v[e] * v[e];
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    v[e] = act ? v[e] * r * ldg(w.kv_norm + k + e) : 0.f;
+    am = fmaxf(am, fabsf(v[e]));
+  }
+  am = block_max(am, red);
+  const int pos = ldg(p.pos + m);
+  if (pos < 0) return;  // pad row: no KV write
+  const float sc = am / 448.0f;
+  uint8_t *rec = nullptr;
+  if (threadIdx.x == 0) rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
+  __syncthreads();
+  if (threadIdx.x == 0) red[8] = __uint_as_float((uint32_t)(rec ? 1u : 0u));
+  __syncthreads();
+  if (red[8] == 0.f) return;
+  rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; e++) stg(rec + k + e, sc > 0.f ? (uint8_t)f32_to_e4m3(v[e] / sc) : (uint8_t)0);
+  }
+  if (threadIdx.x == 0) st16(rec + p.D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
+}
+
+__device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red) {
+  const int eq = row_elems(p.qr), ekv = row_elems(p.D);
+  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+    switch (eq) {
+      case 1: qpost_row<1>(p, w, m, red); break;
+      case 2: qpost_row<2>(p, w, m, red); break;
+      case 4: qpost_row<4>(p, w, m, red); break;
+      case 8: qpost_row<8>(p, w, m, red); break;
+      default: qpost_row<16>(p, w, m, red); break;
     }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + p.eps);
-    float am = 0.f;
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const int k = 4 * cx.lane + 256 * c;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        v[c][e] = k < D ? v[c][e] * r * w.kv_norm[k + e] : 0.f;
-        am = fmaxf(am, fabsf(v[c][e]));
-      }
+    switch (ekv) {
+      case 1: kvpost_row<1>(p, w, kv, m, red); break;
+      default: kvpost_row<2>(p, w, kv, m, red); break;
     }
-    am = wave_max(am);
-    const float sc = am / 448.0f;
-    uint8_t *rec = record_ptr(p, kv, slot_of(p, kv, kv.row_req[m], pos));
-    if (!rec) continue;
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const int k = 4 * cx.lane + 256 * c;
-      if (k < D) {
-        uint32_t code = 0;
-        if (sc > 0.f) {
-#pragma unroll
-          for (int e = 0; e < 4; e++) code |= f32_to_e4m3(v[c][e] / sc) << (8 * e);
-        }
-        *reinterpret_cast<uint32_t *>(rec + k) = code;
-      }
-    }
-    if (cx.lane == 0) st16(rec + D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
   }
 }
 
 // ============================================================== attention
 
 template <int V>
-__device__ __forceinline__ void load_codes(const uint8_t *p, float out[V]) {
+__device__ __forceinline__ void decode_codes(uint64_t c, float out[V]) {
   if constexpr (V == 8) {
-    const v2u c = *reinterpret_cast<const v2u *>(p);
-    const v2f a = cvt_fp8x2_f32<false>(c[0]), b = cvt_fp8x2_f32<true>(c[0]);
-    const v2f d = cvt_fp8x2_f32<false>(c[1]), e = cvt_fp8x2_f32<true>(c[1]);
+    const v2f a = cvt_fp8x2_f32<false>((uint32_t)c), b = cvt_fp8x2_f32<true>((uint32_t)c);
+    const v2f d = cvt_fp8x2_f32<false>((uint32_t)(c >> 32)), e = cvt_fp8x2_f32<true>((uint32_t)(c >> 32));
     out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
     out[4] = d[0]; out[5] = d[1]; out[6] = e[0]; out[7] = e[1];
   } else if constexpr (V == 4) {
-    const uint32_t c = *reinterpret_cast<const uint32_t *>(p);
-    const v2f a = cvt_fp8x2_f32<false>(c), b = cvt_fp8x2_f32<true>(c);
+    const v2f a = cvt_fp8x2_f32<false>((uint32_t)c), b = cvt_fp8x2_f32<true>((uint32_t)c);
     out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
   } else if constexpr (V == 2) {
-    const uint32_t c = *reinterpret_cast<const uint16_t *>(p);
-    const v2f a = cvt_fp8x2_f32<false>(c);
+    const v2f a = cvt_fp8x2_f32<false>((uint32_t)c);
     out[0] = a[0]; out[1] = a[1];
   } else {
-    out[0] = e4m3_to_f32(*p);
+    out[0] = e4m3_to_f32((uint32_t)c & 0xFFu);
   }
+}
+
+template <int V>
+__device__ __forceinline__ uint64_t load_codes(const uint8_t *p) {
+  if constexpr (V == 8) return ldg(reinterpret_cast<const uint64_t *>(p));
+  else if constexpr (V == 4) return ldg(reinterpret_cast<const uint32_t *>(p));
+  else if constexpr (V == 2) return ldg(reinterpret_cast<const uint16_t *>(p));
+  else return ldg(p);
 }
 
 // One (row, head, split): scores q . k / sqrt(D) over up to 32 keys of the row's key set,
 // with k = v = scale * e4m3(codes) of the record; partial max, sum of exponentials and
-// exponential-weighted sum of values.  Lane l holds dims [V*l, V*l + V).
+// exponential-weighted sum of values.  Lane j < 32 resolves key j's record; then every
+// lane loads its V dims of all 32 keys at once.  Lane l holds dims [V*l, V*l + V).
 template <int V>
-__device__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane) {
+__device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane) {
   const int D = p.D, H = p.H;
-  const int pos = p.pos[m];
+  const int pos = ldg(p.pos + m);
   const size_t item = ((size_t)m * H + hh) * p.S + sp;
-  float *o_out = p.s.att_o + item * D;
-  float *ml = p.s.att_ml + item * 2;
   int nk, lo = 0;
   if (p.swa > 0) {
     nk = p.swa;
@@ -158,73 +191,97 @@ __device__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int 
     lo = pos - p.W + 1 < 0 ? 0 : pos - p.W + 1;
     nk = pos - lo + 1;
   }
-  const int j0 = sp * kSplitKeys, j1 = min(nk, j0 + kSplitKeys);
+  const int j0 = sp * kSplitKeys;
+  // lane j < 32: the record of key j0 + j (or null)
+  const uint8_t *myrec = nullptr;
+  if (lane < kSplitKeys && j0 + lane < nk) {
+    int64_t slot;
+    if (p.swa > 0) {
+      slot = ldg(kv.key_table + (size_t)m * p.swa + j0 + lane);
+      myrec = slot < 0 ? nullptr : record_ptr(p, kv, slot);
+    } else {
+      myrec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), lo + j0 + lane));
+    }
+  }
+  const float mysc = myrec ? ldg(reinterpret_cast<const float *>(myrec + D)) : 0.f;
   const int nks = p.qr / p.pl.kc_qb;
   const size_t qstride = (size_t)p.M * H * D;
   const float *qp = p.s.p_q + (size_t)m * H * D + (size_t)hh * D + lane * V;
   float q[V];
 #pragma unroll
-  for (int v = 0; v < V; v++) q[v] = 0.f;
-  for (int ks = 0; ks < nks; ks++) {
+  for (int v = 0; v < V; v++) q[v] = ldg(qp + v);
+  for (int ks = 1; ks < nks; ks++) {
 #pragma unroll
-    for (int v = 0; v < V; v++) q[v] += qp[ks * qstride + v];
+    for (int v = 0; v < V; v++) q[v] += ldg(qp + ks * qstride + v);
   }
-  const int req = kv.row_req[m];
-  auto rec_of = [&](int j) -> const uint8_t * {
-    int64_t slot;
-    if (p.swa > 0) {
-      slot = kv.key_table[(size_t)m * p.swa + j];
-      if (slot < 0) return nullptr;
-    } else {
-      slot = slot_of(p, kv, req, lo + j);
-    }
-    return record_ptr(p, kv, slot);
-  };
+  const uint64_t recbits = reinterpret_cast<uint64_t>(myrec);
+  constexpr int HALF = kSplitKeys / 2;
+  // scores, 16 keys at a time: every lane loads its V dims of the 16 keys at once
   float my = -INFINITY;
-  for (int j = j0; j < j1; j++) {
-    const uint8_t *rec = rec_of(j);
-    if (!rec) continue;
-    float c[V];
-    load_codes<V>(rec + lane * V, c);
-    const float sc = *reinterpret_cast<const float *>(rec + D);
-    float d = 0.f;
 #pragma unroll
-    for (int v = 0; v < V; v++) d += q[v] * c[v];
-    d = wave_sum(d) * sc * p.attn_scale;
-    if (lane == j - j0) my = d;
+  for (int h0 = 0; h0 < kSplitKeys; h0 += HALF) {
+    uint64_t codes[HALF];
+#pragma unroll
+    for (int j = 0; j < HALF; j++) {
+      const uint64_t rb = ((uint64_t)__shfl((unsigned)(recbits >> 32), h0 + j, kWave) << 32) |
+                          (uint64_t)__shfl((unsigned)recbits, h0 + j, kWave);
+      codes[j] = rb ? load_codes<V>(reinterpret_cast<const uint8_t *>(rb) + lane * V) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < HALF; j++) {
+      float c[V];
+      decode_codes<V>(codes[j], c);
+      float d = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; v++) d += q[v] * c[v];
+      d = wave_sum(d);
+      if (lane == h0 + j) my = myrec ? d * mysc * p.attn_scale : -INFINITY;
+    }
   }
   const float mx = wave_max(my);
   const float pj = my == -INFINITY ? 0.f : expf(my - mx);
   const float l = wave_sum(pj);
+  const float f = pj * mysc;
+  // output: the same records again (now cache hits), weighted by exp(score - max) * scale
   float o[V];
 #pragma unroll
   for (int v = 0; v < V; v++) o[v] = 0.f;
-  for (int j = j0; j < j1; j++) {
-    const float pw = __shfl(pj, j - j0, kWave);
-    if (pw == 0.f) continue;
-    const uint8_t *rec = rec_of(j);
-    if (!rec) continue;
-    float c[V];
-    load_codes<V>(rec + lane * V, c);
-    const float f = pw * *reinterpret_cast<const float *>(rec + D);
 #pragma unroll
-    for (int v = 0; v < V; v++) o[v] += f * c[v];
-  }
+  for (int h0 = 0; h0 < kSplitKeys; h0 += HALF) {
+    uint64_t codes[HALF];
 #pragma unroll
-  for (int v = 0; v < V; v++) o_out[lane * V + v] = o[v];
-  if (lane == 0) {
-    ml[0] = mx;
-    ml[1] = l;
+    for (int j = 0; j < HALF; j++) {
+      const uint64_t rb = ((uint64_t)__shfl((unsigned)(recbits >> 32), h0 + j, kWave) << 32) |
+                          (uint64_t)__shfl((unsigned)recbits, h0 + j, kWave);
+      codes[j] = rb ? load_codes<V>(reinterpret_cast<const uint8_t *>(rb) + lane * V) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < HALF; j++) {
+      const float fj = __shfl(f, h0 + j, kWave);
+      float c[V];
+      decode_codes<V>(codes[j], c);
+#pragma unroll
+      for (int v = 0; v < V; v++) o[v] += fj * c[v];
+    }
   }
+  float *o_out = p.s.att_o + item * D + lane * V;
+  if constexpr (V >= 4) {
+#pragma unroll
+    for (int v = 0; v < V; v += 4) st_f4(o_out + v, make_float4(o[v], o[v + 1], o[v + 2], o[v + 3]));
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; v++) stg(o_out + v, o[v]);
+  }
+  if (lane == 0) st_f2(p.s.att_ml + item * 2, make_float2(mx, l));
 }
 
 template <int V>
-__device__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv) {
+__device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv) {
   const int T = p.M * p.H * p.S;
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int m = t / (p.H * p.S), rem = t - m * p.H * p.S;
     const int hh = rem / p.S, sp = rem - hh * p.S;
-    if (p.pos[m] < 0) continue;
+    if (ldg(p.pos + m) < 0) continue;
     attn_item<V>(p, kv, m, hh, sp, cx.lane);
   }
 }
@@ -232,174 +289,146 @@ __device__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv)
 // Log-sum-exp combine of the splits of one (row, head), then MXFP8 of the output
 // (32-blocks span 32/V lanes).  Pad rows give zeros.
 template <int V>
-__device__ void st_combine_v(const Params &p, const Ctx &cx) {
+__device__ __forceinline__ void st_combine_v(const Params &p, const Ctx &cx) {
+  constexpr int SMAX = 8;
   const int T = p.M * p.H, D = p.D, S = p.S;
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int m = t / p.H, hh = t - m * p.H;
     float o[V];
 #pragma unroll
     for (int v = 0; v < V; v++) o[v] = 0.f;
-    if (p.pos[m] >= 0) {
+    if (ldg(p.pos + m) >= 0) {
       const size_t item0 = ((size_t)m * p.H + hh) * S;
-      const float *ml = p.s.att_ml + item0 * 2;
-      float mx = -INFINITY;
-      for (int s = 0; s < S; s++) mx = fmaxf(mx, ml[2 * s]);
-      float L = 0.f;
-      for (int s = 0; s < S; s++) {
-        if (!(ml[2 * s + 1] > 0.f)) continue;
-        const float e = expf(ml[2 * s] - mx);
-        L += ml[2 * s + 1] * e;
-        const float *os = p.s.att_o + (item0 + s) * D + cx.lane * V;
+      float ms[SMAX], ls[SMAX], os[SMAX][V];
 #pragma unroll
-        for (int v = 0; v < V; v++) o[v] += os[v] * e;
+      for (int s = 0; s < SMAX; s++) {
+        const int sc = s < S ? s : S - 1;
+        const float2 ml = ld_f2(p.s.att_ml + (item0 + sc) * 2);
+        ms[s] = s < S ? ml.x : -INFINITY;
+        ls[s] = s < S ? ml.y : 0.f;
+        const float *op = p.s.att_o + (item0 + sc) * D + cx.lane * V;
+#pragma unroll
+        for (int v = 0; v < V; v++) os[s][v] = ldg(op + v);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < SMAX; s++) mx = fmaxf(mx, ms[s]);
+      float L = 0.f;
+#pragma unroll
+      for (int s = 0; s < SMAX; s++) {
+        if (!(ls[s] > 0.f)) continue;
+        const float e = expf(ms[s] - mx);
+        L += ls[s] * e;
+#pragma unroll
+        for (int v = 0; v < V; v++) o[v] += os[s][v] * e;
       }
       if (L > 0.f) {
 #pragma unroll
         for (int v = 0; v < V; v++) o[v] = o[v] / L;
       }
     }
-    float am = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; v++) am = fmaxf(am, fabsf(o[v]));
-    am = group_max<32 / V>(am);
-    const uint32_t X = mx_e4m3_exponent(am);
-    const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
-    uint16_t *dst = p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + cx.lane * V;
-#pragma unroll
-    for (int v = 0; v < V; v++) dst[v] = (uint16_t)f32_to_bf16(e4m3_to_f32(f32_to_e4m3(o[v] * inv)) * sc);
+    mx_quant_dequant<V>(o);
+    store_bf16<V>(p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + cx.lane * V, o);
   }
 }
 
 // wo_a output: sum the split-K partials, then MXFP8
-__device__ void st_t_quant(const Params &p, const Ctx &cx) {
-  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa;
-  const size_t pstride = (size_t)p.M * N;
-  for (int m = cx.gw; m < p.M; m += cx.nw) {
-    const float *base = p.s.p_t + (size_t)m * N;
-    auto load4 = [&](int k) {
-      float4 a = *reinterpret_cast<const float4 *>(base + k);
-      for (int ks = 1; ks < nks; ks++) {
-        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-      return a;
-    };
-    wave_row_mxq(load4, N, nullptr, 0.f, p.s.tb + (size_t)m * N, cx.lane);
+template <int E>
+__device__ __forceinline__ void st_t_quant_e(const Params &p) {
+  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa, k = threadIdx.x * E;
+  const bool act = k < N;
+  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+    float v[E];
+    if (act)
+      load_sum_f32<E>(p.s.p_t + (size_t)m * N + k, (size_t)p.M * N, nks, v);
+    else
+#pragma unroll
+      for (int e = 0; e < E; e++) v[e] = 0.f;
+    mx_quant_dequant<E>(v);
+    if (act) store_bf16<E>(p.s.tb + (size_t)m * N + k, v);
   }
 }
 
 // wo_b output a (sum of partials).  Attention-only steps write bf16(a).  Full steps:
 // hres = bf16(x + a), u = bf16(RMSNorm_ffn(hres)).  Pad rows give zeros.
-__device__ void st_ffn_norm(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *xin, bool last) {
-  const int h = p.h, nks = p.orr / p.pl.kc_ob;
-  const size_t pstride = (size_t)p.M * h;
-  const int nb = h >> 5;
-  for (int m = cx.gw; m < p.M; m += cx.nw) {
-    const bool live = p.pos[m] >= 0;
-    const float *base = p.s.p_a + (size_t)m * h;
-    const uint16_t *xr = xin + (size_t)m * h;
-    auto a4 = [&](int k) {
-      float4 a = *reinterpret_cast<const float4 *>(base + k);
-      for (int ks = 1; ks < nks; ks++) {
-        const float4 b = *reinterpret_cast<const float4 *>(base + ks * pstride + k);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-      return a;
-    };
-    auto hres4 = [&](int k, float hr[4]) {
-      const float4 a = a4(k);
-      const v2u xv = *reinterpret_cast<const v2u *>(xr + k);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      const float xf[4] = {bf16_to_f32(xv[0] & 0xFFFFu), bf16_to_f32(xv[0] >> 16), bf16_to_f32(xv[1] & 0xFFFFu),
-                           bf16_to_f32(xv[1] >> 16)};
+template <int E>
+__device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, bool last, float *red) {
+  const int h = p.h, nks = p.orr / p.pl.kc_ob, k = threadIdx.x * E;
+  const bool act = k < h;
+  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+    const bool live = ldg(p.pos + m) >= 0;
+    float a[E], hr[E];
+    if (act) {
+      load_sum_f32<E>(p.s.p_a + (size_t)m * h + k, (size_t)p.M * h, nks, a);
+      load_bf16<E>(xin + (size_t)m * h + k, hr);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; e++) hr[e] = live ? bf16_to_f32(f32_to_bf16(xf[e] + av[e])) : 0.f;
-    };
-    auto pack = [](const float f[4]) {
-      return v2u{f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16), f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16)};
-    };
+      for (int e = 0; e < E; e++) a[e] = hr[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      a[e] = live ? a[e] : 0.f;
+      hr[e] = live ? bf16_to_f32(f32_to_bf16(hr[e] + a[e])) : 0.f;
+    }
+    const size_t off = (size_t)m * h + k;
     if (p.mode == kModeAttn) {
-      for (int k = cx.lane * 4; k < h; k += 4 * kWave) {
-        const float4 a = a4(k);
-        const float f[4] = {live ? a.x : 0.f, live ? a.y : 0.f, live ? a.z : 0.f, live ? a.w : 0.f};
-        *reinterpret_cast<v2u *>(p.out + (size_t)m * h + k) = pack(f);
-      }
+      if (act) store_bf16<E>(p.out + off, a);
       continue;
     }
     float ss = 0.f;
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      const int blk = b0 + (cx.lane >> 3);
-      if (blk >= nb) continue;
-      const int k = blk * 32 + (cx.lane & 7) * 4;
-      float hr[4];
-      hres4(k, hr);
 #pragma unroll
-      for (int e = 0; e < 4; e++) ss += hr[e] * hr[e];
-      if (last) {
-        if (p.taps.hres) *reinterpret_cast<v2u *>((uint16_t *)p.taps.hres + (size_t)m * h + k) = pack(hr);
-        if (p.taps.attn_out) {
-          const float4 a = a4(k);
-          const float f[4] = {live ? a.x : 0.f, live ? a.y : 0.f, live ? a.z : 0.f, live ? a.w : 0.f};
-          *reinterpret_cast<v2u *>((uint16_t *)p.taps.attn_out + (size_t)m * h + k) = pack(f);
-        }
-      }
-      *reinterpret_cast<v2u *>(p.s.hres + (size_t)m * h + k) = pack(hr);
-    }
-    ss = wave_sum(ss);
+    for (int e = 0; e < E; e++) ss += hr[e] * hr[e];
+    ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)h + p.eps);
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      const int blk = b0 + (cx.lane >> 3);
-      if (blk >= nb) continue;
-      const int k = blk * 32 + (cx.lane & 7) * 4;
-      float hr[4], uu[4];
-      hres4(k, hr);
+    if (!act) continue;
+    store_bf16<E>(p.s.hres + off, hr);
+    if (last && p.taps.hres) store_bf16<E>((uint16_t *)p.taps.hres + off, hr);
+    if (last && p.taps.attn_out) store_bf16<E>((uint16_t *)p.taps.attn_out + off, a);
+    float uu[E];
 #pragma unroll
-      for (int e = 0; e < 4; e++) uu[e] = live ? hr[e] * r * w.ffn_norm[k + e] : 0.f;
-      const v2u pk = pack(uu);
-      *reinterpret_cast<v2u *>(p.s.u + (size_t)m * h + k) = pk;
-      if (last && p.taps.moe_in) *reinterpret_cast<v2u *>((uint16_t *)p.taps.moe_in + (size_t)m * h + k) = pk;
-    }
+    for (int e = 0; e < E; e++) uu[e] = live ? hr[e] * r * ldg(w.ffn_norm + k + e) : 0.f;
+    store_bf16<E>(p.s.u + off, uu);
+    if (last && p.taps.moe_in) store_bf16<E>((uint16_t *)p.taps.moe_in + off, uu);
   }
 }
 
 // ============================================================== MoE
 
-// f32 router logits of one expert for all rows: lane-strided dot products, then a wave sum
-__device__ void router_task(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e, int lane) {
-  constexpr int MR = DSL_MAX_ROWS;
-  float acc[MR];
-#pragma unroll
-  for (int m = 0; m < MR; m++) acc[m] = 0.f;
+constexpr int kRouterRows = 4;
+
+// f32 router logits of one expert for up to 4 rows: lane-strided dot products over the
+// whole hidden dimension (the expert's weight row is loaded once), then wave sums.
+__device__ __forceinline__ void router_task(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e, int m0,
+                            int lane) {
+  float acc[kRouterRows] = {0.f, 0.f, 0.f, 0.f};
   const float *wrow = Wr + (size_t)e * p.h;
   for (int k = lane * 4; k < p.h; k += 4 * kWave) {
-    const float4 w4 = *reinterpret_cast<const float4 *>(wrow + k);
+    const float4 w4 = ld_f4(wrow + k);
 #pragma unroll
-    for (int m = 0; m < MR; m++) {
-      if (m < p.M) {
-        const v2u uv = *reinterpret_cast<const v2u *>(u + (size_t)m * p.h + k);
-        acc[m] += w4.x * bf16_to_f32(uv[0] & 0xFFFFu) + w4.y * bf16_to_f32(uv[0] >> 16) +
-                  w4.z * bf16_to_f32(uv[1] & 0xFFFFu) + w4.w * bf16_to_f32(uv[1] >> 16);
-      }
+    for (int r = 0; r < kRouterRows; r++) {
+      const int m = m0 + r < p.M ? m0 + r : p.M - 1;
+      const v2u uv = ldg(reinterpret_cast<const v2u *>(u + (size_t)m * p.h + k));
+      acc[r] += w4.x * bf16_to_f32(uv[0] & 0xFFFFu) + w4.y * bf16_to_f32(uv[0] >> 16) +
+                w4.z * bf16_to_f32(uv[1] & 0xFFFFu) + w4.w * bf16_to_f32(uv[1] >> 16);
     }
   }
 #pragma unroll
-  for (int m = 0; m < MR; m++) {
-    if (m < p.M) {
-      const float s = wave_sum(acc[m]);
-      if (lane == 0) p.s.logits[(size_t)m * p.E + e] = s;
-    }
+  for (int r = 0; r < kRouterRows; r++) {
+    const float s = wave_sum(acc[r]);
+    if (lane == 0 && m0 + r < p.M) stg(p.s.logits + (size_t)(m0 + r) * p.E + e, s);
   }
 }
 
-// Router logits (E tasks) and the shared expert's gate/up partials, together: both
-// read only the MoE input.
-__device__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
-  const int TR = p.E;
+// Router logits ((expert, 4-row group) tasks) and the shared expert's gate/up partials,
+// together: both read only the MoE input.
+__device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
+  const int groups = (p.M + kRouterRows - 1) / kRouterRows;
+  const int TR = p.E * groups;
   const int Nsh = 2 * p.Is;
   const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
   for (int t = cx.gw; t < TR + TS; t += cx.nw) {
     if (t < TR)
-      router_task(p, w.w_router, u, t, cx.lane);
+      router_task(p, w.w_router, u, t % p.E, (t / p.E) * kRouterRows, cx.lane);
     else
       linear_task<kW8B128>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u, p.M,
                            p.s.p_sh);
@@ -409,12 +438,12 @@ __device__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weigh
 // Top-k of every live row (ties to the lower id, descending order, weights = softmax of
 // the selected logits), then the distinct-expert list and the (row, slot) -> pair map
 // ordered by expert id.  Every block builds the same routing in its own LDS.
-__device__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
+__device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
   const int k = p.k, E = p.E;
   for (int e = threadIdx.x; e < 128; e += kThreads) R.cnt[e] = 0;
   __syncthreads();
   for (int m = cx.wave; m < p.M; m += kWavesPerBlock) {
-    const bool live = all_live || p.pos[m] >= 0;
+    const bool live = all_live || ldg(p.pos + m) >= 0;
     if (!live) {
       if (cx.lane < k) {
         R.ids[m * k + cx.lane] = -1;
@@ -423,8 +452,8 @@ __device__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool a
       continue;
     }
     const float *lg = p.s.logits + (size_t)m * E;
-    float l0 = cx.lane < E ? lg[cx.lane] : -INFINITY;
-    float l1 = cx.lane + 64 < E ? lg[cx.lane + 64] : -INFINITY;
+    float l0 = cx.lane < E ? ldg(lg + cx.lane) : -INFINITY;
+    float l1 = cx.lane + 64 < E ? ldg(lg + cx.lane + 64) : -INFINITY;
     int myid = -1;
     float myval = -INFINITY;
     for (int j = 0; j < k; j++) {
@@ -487,28 +516,28 @@ __device__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool a
 }
 
 // Shared SwiGLU over all (row, column): z = bf16(swiglu_clamp(gate, up))
-__device__ void st_shared_swiglu(const Params &p, bool all_live) {
+__device__ __forceinline__ void st_shared_swiglu(const Params &p, bool all_live) {
   const int Is = p.Is, nks = p.h / p.pl.kc_sh13;
   const size_t pstride = (size_t)p.M * 2 * Is;
   const int total = p.M * Is;
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
     const int m = idx / Is, n = idx - m * Is;
     float z = 0.f;
-    if (all_live || p.pos[m] >= 0) {
+    if (all_live || ldg(p.pos + m) >= 0) {
       const float *b = p.s.p_sh + (size_t)m * 2 * Is;
       float g = 0.f, u = 0.f;
       for (int ks = 0; ks < nks; ks++) {
-        g += b[ks * pstride + n];
-        u += b[ks * pstride + Is + n];
+        g += ldg(b + ks * pstride + n);
+        u += ldg(b + ks * pstride + Is + n);
       }
       z = swiglu_clamp(g, u, p.lim);
     }
-    p.s.zsh[idx] = (uint16_t)f32_to_bf16(z);
+    stg(p.s.zsh + idx, (uint16_t)f32_to_bf16(z));
   }
 }
 
 template <int NCG>
-__device__ void routed_gate_up_task(const Params &p, const dsl_weights &w, const Routing &R, const uint16_t *u,
+__device__ __forceinline__ void routed_gate_up_task(const Params &p, const dsl_weights &w, const Routing &R, const uint16_t *u,
                                     int e, int p0, int ce, int tile, int lane) {
   const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
   const uint8_t *W = w.ex_w13 + (size_t)e * (2 * I) * (h >> 1);
@@ -523,21 +552,25 @@ __device__ void routed_gate_up_task(const Params &p, const dsl_weights &w, const
     xrow[c] = u + (size_t)(xok[c] ? R.pair_row[p0 + j] : 0) * h;
     acc[0][c] = acc[1][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  const int n0[2] = {tile * 16, I + tile * 16};
-  bf16_tiles<kW4, 2, NCG>(W, S8, nullptr, h, n0, 0, h, xrow, xok, acc, lane);
+  const WStream ws[2] = {wstream<kW4>(W, S8, nullptr, h, tile * 16 + i, 0, g),
+                         wstream<kW4>(W, S8, nullptr, h, I + tile * 16 + i, 0, g)};
+  tiles<kW4, 2, NCG>(ws, h >> 7, xrow, xok, 32 * g, g, acc);
 #pragma unroll
   for (int c = 0; c < NCG; c++) {
     const int j = 16 * c + i;
     if (j < ce) {
       uint16_t *z = p.s.zr + (size_t)(p0 + j) * I + tile * 16 + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 4; r++) z[r] = (uint16_t)f32_to_bf16(swiglu_clamp(acc[0][c][r], acc[1][c][r], p.lim));
+      const v2u pk = {f32_to_bf16(swiglu_clamp(acc[0][c][0], acc[1][c][0], p.lim)) |
+                          (f32_to_bf16(swiglu_clamp(acc[0][c][1], acc[1][c][1], p.lim)) << 16),
+                      f32_to_bf16(swiglu_clamp(acc[0][c][2], acc[1][c][2], p.lim)) |
+                          (f32_to_bf16(swiglu_clamp(acc[0][c][3], acc[1][c][3], p.lim)) << 16)};
+      stg(reinterpret_cast<v2u *>(z), pk);
     }
   }
 }
 
 template <int NCG>
-__device__ void routed_down_task(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile, int lane) {
+__device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile, int lane) {
   const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
   const uint8_t *W = w.ex_wd + (size_t)e * h * (I >> 1);
   const uint8_t *S8 = w.ex_wd_s + (size_t)e * h * (I >> 5);
@@ -551,28 +584,25 @@ __device__ void routed_down_task(const Params &p, const dsl_weights &w, int e, i
     xrow[c] = p.s.zr + (size_t)(p0 + (xok[c] ? j : 0)) * I;
     acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  const int n0[1] = {tile * 16};
-  bf16_tiles<kW4, 1, NCG>(W, S8, nullptr, I, n0, 0, I, xrow, xok, acc, lane);
+  const WStream ws[1] = {wstream<kW4>(W, S8, nullptr, I, tile * 16 + i, 0, g)};
+  tiles<kW4, 1, NCG>(ws, I >> 7, xrow, xok, 32 * g, g, acc);
 #pragma unroll
   for (int c = 0; c < NCG; c++) {
     const int j = 16 * c + i;
-    if (j < ce) {
-      float *y = p.s.y + (size_t)(p0 + j) * h + tile * 16 + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 4; r++) y[r] = acc[0][c][r];
-    }
+    if (j < ce) stg(reinterpret_cast<v4f *>(p.s.y + (size_t)(p0 + j) * h + tile * 16 + 4 * g), acc[0][c]);
   }
 }
 
 // Routed gate/up tasks (selected expert, 16-row tile of gate and of up) from the queue
-__device__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
+__device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                   const uint16_t *u, unsigned *ctr) {
-  const int tiles = p.I >> 4;
-  const int T = R.nd * tiles;
+  const int tiles_n = p.I >> 4;
+  const int T = R.nd * tiles_n;
+  TaskQueue tq(ctr, cx);
   for (;;) {
-    const int t = claim_task(ctr, cx.lane);
+    const int t = tq.take(cx.lane);
     if (t >= T) break;
-    const int q = t / tiles, tile = t - q * tiles;
+    const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
     if (ncg == 1)
@@ -585,16 +615,17 @@ __device__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weig
 }
 
 // Shared down partials (static split), then routed down tasks from the queue
-__device__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R, unsigned *ctr) {
+__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R, unsigned *ctr) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
   for (int t = cx.gw; t < TS; t += cx.nw)
     linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
-  const int tiles = p.h >> 4;
-  const int T = R.nd * tiles;
+  const int tiles_n = p.h >> 4;
+  const int T = R.nd * tiles_n;
+  TaskQueue tq(ctr, cx);
   for (;;) {
-    const int t = claim_task(ctr, cx.lane);
+    const int t = tq.take(cx.lane);
     if (t >= T) break;
-    const int q = t / tiles, tile = t - q * tiles;
+    const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
     if (ncg == 1)
@@ -608,51 +639,88 @@ __device__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, co
 
 // m = shared + sum_j w_j y_j in float32 (shared first, slots in emission order);
 // MoE steps write bf16(m), full steps bf16(hres + m).
-__device__ void st_combine_out(const Params &p, const Routing &R, bool moe_mode, bool last, uint16_t *dst) {
+__device__ __forceinline__ void st_combine_out(const Params &p, const Routing &R, bool moe_mode, bool last, uint16_t *dst) {
   const int h = p.h, k = p.k, nks = p.Is / p.pl.kc_shd;
   const size_t pstride = (size_t)p.M * h;
   const int total = p.M * h;
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
     const int m = idx / h, n = idx - m * h;
-    const bool live = moe_mode || p.pos[m] >= 0;
+    const bool live = moe_mode || ldg(p.pos + m) >= 0;
     float mo = 0.f;
     if (live) {
-      for (int ks = 0; ks < nks; ks++) mo += p.s.p_shd[ks * pstride + idx];
-      for (int j = 0; j < k; j++) mo = fmaf(R.w[m * k + j], p.s.y[(size_t)R.pair[m * k + j] * h + n], mo);
+      for (int ks = 0; ks < nks; ks++) mo += ldg(p.s.p_shd + ks * pstride + idx);
+      for (int j = 0; j < k; j++) mo = fmaf(R.w[m * k + j], ldg(p.s.y + (size_t)R.pair[m * k + j] * h + n), mo);
     }
     if (moe_mode) {
-      dst[idx] = live ? (uint16_t)f32_to_bf16(mo) : 0;
+      stg(dst + idx, live ? (uint16_t)f32_to_bf16(mo) : (uint16_t)0);
     } else {
-      dst[idx] = live ? (uint16_t)f32_to_bf16(bf16_to_f32(p.s.hres[idx]) + mo) : 0;
-      if (last && p.taps.moe_out) ((uint16_t *)p.taps.moe_out)[idx] = live ? (uint16_t)f32_to_bf16(mo) : 0;
+      stg(dst + idx, live ? (uint16_t)f32_to_bf16(bf16_to_f32(ldg(p.s.hres + idx)) + mo) : (uint16_t)0);
+      if (last && p.taps.moe_out) stg((uint16_t *)p.taps.moe_out + idx, live ? (uint16_t)f32_to_bf16(mo) : (uint16_t)0);
     }
   }
 }
 
 // ============================================================== the persistent launch
 
-__global__ void __launch_bounds__(kThreads, 2) dsl_layer_kernel(Params p) {
+// One layer's weight descriptors from device memory (global loads of its pointer words)
+__device__ __forceinline__ dsl_weights load_weights(const dsl_weights *src) {
+  static_assert(sizeof(dsl_weights) % 8 == 0, "descriptor size");
+  dsl_weights w;
+  const uint64_t *s = reinterpret_cast<const uint64_t *>(src);
+  uint64_t *d = reinterpret_cast<uint64_t *>(&w);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(dsl_weights) / 8); i++) d[i] = ldg(s + i);
+  return w;
+}
+
+// Block 0 stamps the device wall clock at the start, after every grid barrier and at
+// the end of a launch when tracing is on (one entry per stage boundary).
+struct Tracer {
+  unsigned long long *buf;
+  int n = 0;
+  __device__ __forceinline__ void mark() {
+    if (buf && blockIdx.x == 0 && threadIdx.x == 0) buf[n] = wall_clock64();
+    n++;
+  }
+};
+
+__global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p) {
   __shared__ Routing R;
+  __shared__ float red[16];
   const Ctx cx = make_ctx();
   SyncWords *sw = p.sync;
   const unsigned nb = gridDim.x;
   if (blockIdx.x == 0 && threadIdx.x < 64)
-    __hip_atomic_store(&sw->tasks[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(&sw->tasks[threadIdx.x]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool moe_mode = p.mode == kModeMoe;
+  Tracer tr{p.trace};
+  tr.mark();
   for (int l = 0; l < p.n_layers; l++) {
-    const dsl_weights w = p.w[l];
-    const dsl_kv &kv = p.kv[l];
+    const dsl_weights w = load_weights(p.w + l);
+    // static indices only: a runtime index into the kernel arguments would copy them to
+    // private memory
+    const dsl_kv kv = l == 0 ? p.kv[0] : l == 1 ? p.kv[1] : l == 2 ? p.kv[2] : p.kv[3];
     const bool last = l == p.n_layers - 1;
     const uint16_t *xin = l == 0 ? p.x : p.s.xin;
     if (!moe_mode) {
-      st_attn_norm(p, cx, w, xin);
+      switch (row_elems(p.h)) {
+        case 1: st_attn_norm_e<1>(p, w, xin, red); break;
+        case 2: st_attn_norm_e<2>(p, w, xin, red); break;
+        case 4: st_attn_norm_e<4>(p, w, xin, red); break;
+        case 8: st_attn_norm_e<8>(p, w, xin, red); break;
+        default: st_attn_norm_e<16>(p, w, xin, red); break;
+      }
       grid_barrier(sw, nb);
+      tr.mark();
       linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
       grid_barrier(sw, nb);
-      st_qkv_post(p, cx, w, kv);
+      tr.mark();
+      st_qkv_post(p, w, kv, red);
       grid_barrier(sw, nb);
+      tr.mark();
       linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
       grid_barrier(sw, nb);
+      tr.mark();
       switch (p.D) {
         case 64: st_attention_v<1>(p, cx, kv); break;
         case 128: st_attention_v<2>(p, cx, kv); break;
@@ -660,6 +728,7 @@ __global__ void __launch_bounds__(kThreads, 2) dsl_layer_kernel(Params p) {
         default: st_attention_v<8>(p, cx, kv); break;
       }
       grid_barrier(sw, nb);
+      tr.mark();
       switch (p.D) {
         case 64: st_combine_v<1>(p, cx); break;
         case 128: st_combine_v<2>(p, cx); break;
@@ -667,35 +736,70 @@ __global__ void __launch_bounds__(kThreads, 2) dsl_layer_kernel(Params p) {
         default: st_combine_v<8>(p, cx); break;
       }
       grid_barrier(sw, nb);
+      tr.mark();
       linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
       grid_barrier(sw, nb);
-      st_t_quant(p, cx);
+      tr.mark();
+      switch (row_elems(p.orr)) {
+        case 1: st_t_quant_e<1>(p); break;
+        case 2: st_t_quant_e<2>(p); break;
+        case 4: st_t_quant_e<4>(p); break;
+        case 8: st_t_quant_e<8>(p); break;
+        default: st_t_quant_e<16>(p); break;
+      }
       grid_barrier(sw, nb);
+      tr.mark();
       linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
       grid_barrier(sw, nb);
-      st_ffn_norm(p, cx, w, xin, last);
-      if (p.mode == kModeAttn) return;
+      tr.mark();
+      switch (row_elems(p.h)) {
+        case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
+        case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
+        case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
+        case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
+        default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+      }
+      if (p.mode == kModeAttn) {
+        tr.mark();
+        return;
+      }
       grid_barrier(sw, nb);
+      tr.mark();
     }
     const uint16_t *u = moe_mode ? p.x : p.s.u;
     st_router_shared(p, cx, w, u);
     grid_barrier(sw, nb);
+      tr.mark();
     build_routing(p, cx, R, moe_mode);
+    tr.mark();
+    if (blockIdx.x == 0 && p.taps.layer_ids)
+      for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) stg(p.taps.layer_ids + (size_t)l * p.M * p.k + t, R.ids[t]);
     if (blockIdx.x == 0 && last) {
       for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) {
-        if (p.taps.topk_ids) p.taps.topk_ids[t] = R.ids[t];
-        if (p.taps.topk_w) p.taps.topk_w[t] = R.w[t];
+        if (p.taps.topk_ids) stg(p.taps.topk_ids + t, R.ids[t]);
+        if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
       }
       if (p.taps.logits)
-        for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) p.taps.logits[t] = p.s.logits[t];
+        for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
     }
     st_shared_swiglu(p, moe_mode);
+    tr.mark();
     st_routed_gate_up(p, cx, w, R, u, &sw->tasks[2 * l]);
+    __syncthreads();
+    tr.mark();
     grid_barrier(sw, nb);
+      tr.mark();
     st_down(p, cx, w, R, &sw->tasks[2 * l + 1]);
+    __syncthreads();
+    tr.mark();
     grid_barrier(sw, nb);
+      tr.mark();
     st_combine_out(p, R, moe_mode, last, last ? p.out : p.s.xin);
-    if (!last) grid_barrier(sw, nb);
+    if (!last) {
+      grid_barrier(sw, nb);
+      tr.mark();
+    }
+      tr.mark();
   }
 }
 
@@ -717,8 +821,11 @@ struct dsl_layer {
   Plan plan{};
   dsl_weights *dw = nullptr;  // device copy of the weight descriptors
   SyncWords *sync = nullptr;
+  unsigned long long *trace = nullptr;  // device buffer of kTraceLen stamps when tracing
   WidthScratch wid[DSL_MAX_ROWS + 1];
 };
+
+static constexpr int kTraceLen = 256;
 
 static thread_local std::string g_err;
 
@@ -861,7 +968,7 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   int bpc = 0;
   HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel, kThreads, 0));
   if (bpc < 1) return fail(DSL_EUNSUPPORTED, "the layer kernel cannot be resident on a compute unit");
-  if (bpc > 2) bpc = 2;
+  if (bpc > 1) bpc = 1;
   dsl_layer *L = new dsl_layer();
   L->d = *dims;
   L->dev = dev;
@@ -944,6 +1051,7 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   p.out = (uint16_t *)out;
   if (taps) p.taps = *taps;
   p.sync = L->sync;
+  p.trace = L->trace;
   void *args[] = {&p};
   HIPCHK(hipSetDevice(L->dev));
   HIPCHK(hipLaunchCooperativeKernel((const void *)dsl_layer_kernel, dim3(L->grid), dim3(kThreads), args, 0,
@@ -981,6 +1089,37 @@ int dsl_layer_health(dsl_layer *L) {
   return 0;
 }
 
+int dsl_layer_set_trace(dsl_layer *L, int32_t on) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  HIPCHK(hipSetDevice(L->dev));
+  if (on && !L->trace) {
+    if (hipMalloc((void **)&L->trace, kTraceLen * sizeof(unsigned long long)) != hipSuccess) {
+      L->trace = nullptr;
+      return fail(DSL_ENOMEM, "trace buffer allocation failed");
+    }
+    HIPCHK(hipMemset(L->trace, 0, kTraceLen * sizeof(unsigned long long)));
+  } else if (!on && L->trace) {
+    HIPCHK(hipFree(L->trace));
+    L->trace = nullptr;
+  }
+  return 0;
+}
+
+int dsl_layer_read_trace(dsl_layer *L, double *ns, int32_t n) {
+  if (!L || !ns || n < 0) return fail(DSL_EINVAL, "layer and ns must be set");
+  if (!L->trace) return fail(DSL_EINVAL, "tracing is off");
+  unsigned long long buf[kTraceLen];
+  HIPCHK(hipSetDevice(L->dev));
+  HIPCHK(hipMemcpy(buf, L->trace, sizeof buf, hipMemcpyDeviceToHost));
+  int khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, L->dev));
+  if (khz <= 0) return fail(DSL_EHIP, "device wall clock rate unknown");
+  int cnt = 0;
+  while (cnt < kTraceLen && buf[cnt]) cnt++;
+  for (int i = 0; i < cnt && i < n; i++) ns[i] = (double)(buf[i] - buf[0]) * 1e6 / khz;
+  return cnt < n ? cnt : n;
+}
+
 int dsl_layer_grid(const dsl_layer *L, int32_t *blocks, int32_t *threads) {
   if (!L) return fail(DSL_EINVAL, "layer is NULL");
   if (blocks) *blocks = L->grid;
@@ -993,6 +1132,7 @@ void dsl_layer_destroy(dsl_layer *L) {
   for (auto &w : L->wid)
     if (w.buf) (void)hipFree(w.buf);
   if (L->sync) (void)hipFree(L->sync);
+  if (L->trace) (void)hipFree(L->trace);
   if (L->dw) (void)hipFree(L->dw);
   delete L;
 }

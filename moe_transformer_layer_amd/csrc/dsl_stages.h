@@ -23,7 +23,7 @@
 
 namespace dsl {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kSplitKeys = 32;  // keys per attention split
 
@@ -69,6 +69,7 @@ struct Params {
   dsl_taps taps;
   Scratch s;
   SyncWords *sync;
+  unsigned long long *trace;  // per-stage timestamps of block 0, or null
 };
 
 // Routing of the current layer, rebuilt in LDS by every block after the router.
@@ -94,49 +95,6 @@ __device__ __forceinline__ Ctx make_ctx() {
   return c;
 }
 
-// ============================================================== row helpers (one wave per row)
-
-// MX-quantize one row of n values (n a multiple of 32) to e4m3 with one E8M0 per 32,
-// optionally after RMSNorm with gamma (r = 1/sqrt(mean(v^2) + eps)), and store the
-// dequantized values (exact in bf16).  load4(k) returns values k..k+3.  Lanes work in
-// groups of 8 per 32-block.
-template <class L4>
-__device__ void wave_row_mxq(L4 load4, int n, const float *gamma, float eps, uint16_t *dst, int lane) {
-  float r = 1.0f;
-  if (gamma) {
-    float ss = 0.f;
-    for (int k = lane * 4; k < n; k += 4 * kWave) {
-      float4 v = load4(k);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = wave_sum(ss);
-    r = 1.0f / sqrtf(ss / (float)n + eps);
-  }
-  const int nb = n >> 5;
-  for (int b0 = 0; b0 < nb; b0 += 8) {
-    const int blk = b0 + (lane >> 3);
-    const bool act = blk < nb;
-    const int k = blk * 32 + (lane & 7) * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (act) {
-      float4 t = load4(k);
-      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-      if (gamma) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = v[e] * r * gamma[k + e];
-      }
-    }
-    float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    am = group_max<8>(am);
-    const uint32_t X = mx_e4m3_exponent(am);
-    const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
-    uint32_t b[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) b[e] = f32_to_bf16(e4m3_to_f32(f32_to_e4m3(v[e] * inv)) * sc);
-    if (act) *reinterpret_cast<v2u *>(dst + k) = v2u{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-  }
-}
-
 // ============================================================== linears on the bf16 matrix unit
 
 // Weight formats of the linears
@@ -146,116 +104,367 @@ enum WFmt : int {
   kW4 = 2,      // e2m1 nibbles [N][K/2] + one E8M0 per 32 along K [N][K/32] (routed experts)
 };
 
-// A fragments of one 128-wide K step for weight row n = n0 + (lane % 16): lane group
-// g = lane / 16 decodes K [32g, 32g+32) of the step into 4 x 8 bf16 (MFMA t takes
-// elements 8t..8t+7).  `kk` is the step's first K index.
+// One lane's raw weight bytes for one 128-wide K step: lane (i, g) covers weight row
+// n0 + i, K [32g, 32g+32) of the step (16 bytes of e2m1 or 32 of e4m3).
+struct RawA {
+  v4u a0, a1;
+};
+
+// Per-lane stream of one weight tile: row pointer at this lane's first K byte and the
+// row's scales at the tile's first K block.
+struct WStream {
+  const uint8_t *w;
+  const uint8_t *s8;   // E8M0 of this lane's row (kW4) or tile row (kW8T32), first block of k0
+  const float *s32;    // f32 block scales of the tile (kW8B128), first 128-block of k0
+};
+
 template <int FMT>
-__device__ __forceinline__ void decode_a(const uint8_t *__restrict__ W, const uint8_t *__restrict__ S8, int K, int n,
-                                         int kk, int g, v4u af[4]) {
+__device__ __forceinline__ WStream wstream(const uint8_t *W, const uint8_t *S8, const float *S32, int K, int n,
+                                           int k0, int g) {
+  WStream st;
   if constexpr (FMT == kW4) {
-    const v4u a = ld16(W + (size_t)n * (K >> 1) + ((kk + 32 * g) >> 1));
-    const float sc = e8m0_to_f32(S8[(size_t)n * (K >> 5) + (kk >> 5) + g]);
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-      af[q] = v4u{cvt_fp4x2_bf16<0>(a[q], sc), cvt_fp4x2_bf16<1>(a[q], sc), cvt_fp4x2_bf16<2>(a[q], sc),
-                  cvt_fp4x2_bf16<3>(a[q], sc)};
+    st.w = W + (size_t)n * (K >> 1) + ((k0 + 32 * g) >> 1);
+    st.s8 = S8 + (size_t)n * (K >> 5) + (k0 >> 5);
+    st.s32 = nullptr;
+  } else if constexpr (FMT == kW8T32) {
+    st.w = W + (size_t)n * K + k0 + 32 * g;
+    st.s8 = S8 + (size_t)(n >> 5) * (K >> 5) + (k0 >> 5);
+    st.s32 = nullptr;
   } else {
-    const uint8_t *p = W + (size_t)n * K + kk + 32 * g;
-    const v4u a0 = ld16(p), a1 = ld16(p + 16);
-    float sc = 1.0f;
-    if constexpr (FMT == kW8T32) sc = e8m0_to_f32(S8[(size_t)(n >> 5) * (K >> 5) + (kk >> 5) + g]);
-    af[0] = v4u{cvt_fp8x2_bf16s<false>(a0[0], sc), cvt_fp8x2_bf16s<true>(a0[0], sc), cvt_fp8x2_bf16s<false>(a0[1], sc),
-                cvt_fp8x2_bf16s<true>(a0[1], sc)};
-    af[1] = v4u{cvt_fp8x2_bf16s<false>(a0[2], sc), cvt_fp8x2_bf16s<true>(a0[2], sc), cvt_fp8x2_bf16s<false>(a0[3], sc),
-                cvt_fp8x2_bf16s<true>(a0[3], sc)};
-    af[2] = v4u{cvt_fp8x2_bf16s<false>(a1[0], sc), cvt_fp8x2_bf16s<true>(a1[0], sc), cvt_fp8x2_bf16s<false>(a1[1], sc),
-                cvt_fp8x2_bf16s<true>(a1[1], sc)};
-    af[3] = v4u{cvt_fp8x2_bf16s<false>(a1[2], sc), cvt_fp8x2_bf16s<true>(a1[2], sc), cvt_fp8x2_bf16s<false>(a1[3], sc),
-                cvt_fp8x2_bf16s<true>(a1[3], sc)};
+    st.w = W + (size_t)n * K + k0 + 32 * g;
+    st.s8 = nullptr;
+    st.s32 = S32 + (size_t)(n >> 7) * (K >> 7) + (k0 >> 7);
+  }
+  return st;
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_a(RawA &r, const WStream &ws, int step) {
+  if constexpr (FMT == kW4) {
+    r.a0 = ld16(ws.w + 64 * step);
+  } else {
+    r.a0 = ld16(ws.w + 128 * step);
+    r.a1 = ld16(ws.w + 128 * step + 16);
   }
 }
 
-// NT weight tiles of 16 rows (rows n0[tt] + lane%16) times NCG groups of 16 bf16 activation
-// rows (xrow[c], valid when xok[c]) over K [k0, k0 + kc).  acc[tt][c] lane l holds
-// C[4*(l/16) + r][l%16]: weight row n0[tt] + 4*(l/16) + r, activation row 16c + l%16.
+// Scales of 4 consecutive steps starting at `step` (a multiple of 4): for E8M0 formats
+// the 16 bytes of K blocks [4*step, 4*step + 16) of the lane's scale row (step s, group
+// g is byte 4s + g); for f32 block scales the 4 steps' floats.  Requires 16-byte
+// aligned scale rows (checked by the caller).
+template <int FMT>
+__device__ __forceinline__ v4u load_scales4(const WStream &ws, int step) {
+  if constexpr (FMT == kW8B128)
+    return ld16(ws.s32 + step);
+  else
+    return ld16(ws.s8 + 4 * step);
+}
+// Scale of one step: byte g of word j of a 4-step group, or one step's own byte
+template <int FMT>
+__device__ __forceinline__ float scale_of4(v4u sc4, int j, int g) {
+  if constexpr (FMT == kW8B128)
+    return __uint_as_float(sc4[j]);
+  else
+    return e8m0_to_f32((sc4[j] >> (8 * g)) & 0xFFu);
+}
+template <int FMT>
+__device__ __forceinline__ float scale_of1(const WStream &ws, int step, int g) {
+  if constexpr (FMT == kW8B128)
+    return ldg(ws.s32 + step);
+  else
+    return e8m0_to_f32(ldg(ws.s8 + 4 * step + g));
+}
+
+// Decode one step's raw bytes into 4 x 8 bf16 A fragments (MFMA t takes elements
+// 8t..8t+7).  Power-of-two scales are folded in exactly; the f32 block scale of the
+// shared expert (sc) is applied to the partial sums instead.
+template <int FMT>
+__device__ __forceinline__ void decode_a(const RawA &r, float sc, v4u af[4]) {
+  if constexpr (FMT == kW4) {
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      af[q] = v4u{cvt_fp4x2_bf16<0>(r.a0[q], sc), cvt_fp4x2_bf16<1>(r.a0[q], sc), cvt_fp4x2_bf16<2>(r.a0[q], sc),
+                  cvt_fp4x2_bf16<3>(r.a0[q], sc)};
+  } else {
+    const float s8 = FMT == kW8T32 ? sc : 1.0f;
+    af[0] = v4u{cvt_fp8x2_bf16s<false>(r.a0[0], s8), cvt_fp8x2_bf16s<true>(r.a0[0], s8),
+                cvt_fp8x2_bf16s<false>(r.a0[1], s8), cvt_fp8x2_bf16s<true>(r.a0[1], s8)};
+    af[1] = v4u{cvt_fp8x2_bf16s<false>(r.a0[2], s8), cvt_fp8x2_bf16s<true>(r.a0[2], s8),
+                cvt_fp8x2_bf16s<false>(r.a0[3], s8), cvt_fp8x2_bf16s<true>(r.a0[3], s8)};
+    af[2] = v4u{cvt_fp8x2_bf16s<false>(r.a1[0], s8), cvt_fp8x2_bf16s<true>(r.a1[0], s8),
+                cvt_fp8x2_bf16s<false>(r.a1[1], s8), cvt_fp8x2_bf16s<true>(r.a1[1], s8)};
+    af[3] = v4u{cvt_fp8x2_bf16s<false>(r.a1[2], s8), cvt_fp8x2_bf16s<true>(r.a1[2], s8),
+                cvt_fp8x2_bf16s<false>(r.a1[3], s8), cvt_fp8x2_bf16s<true>(r.a1[3], s8)};
+  }
+}
+
+// B fragments of one step for one group of 16 activation rows: lane (j, g) holds row
+// j's 32 bf16 at K [32g, 32g+32) of the step (rows past the group's end are zero).
+__device__ __forceinline__ void load_b(v4u b[4], const uint16_t *row, bool ok, int k) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) b[t] = ok ? ld16(row + k + 8 * t) : v4u{0, 0, 0, 0};
+}
+
 template <int FMT, int NT, int NCG>
-__device__ void bf16_tiles(const uint8_t *__restrict__ W, const uint8_t *__restrict__ S8,
-                           const float *__restrict__ S32, int K, const int n0[NT], int k0, int kc,
-                           const uint16_t *const xrow[NCG], const bool xok[NCG], v4f acc[NT][NCG], int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const int steps = kc >> 7;
-  for (int s = 0; s < steps; s++) {
-    const int kk = k0 + 128 * s;
-    v4u af[NT][4];
+__device__ __forceinline__ void step_mfma(const v4u af[NT][4], const float bsc[NT], const v4u b[NCG][4],
+                                          v4f acc[NT][NCG]) {
 #pragma unroll
-    for (int tt = 0; tt < NT; tt++) decode_a<FMT>(W, S8, K, n0[tt] + i, kk, g, af[tt]);
+  for (int c = 0; c < NCG; c++) {
 #pragma unroll
-    for (int c = 0; c < NCG; c++) {
-      v4u b[4];
+    for (int tt = 0; tt < NT; tt++) {
+      if constexpr (FMT == kW8B128) {
+        v4f t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; t++) b[t] = xok[c] ? ld16(xrow[c] + kk + 32 * g + 8 * t) : v4u{0, 0, 0, 0};
+        for (int q = 0; q < 4; q++) t = mfma_bf16(af[tt][q], b[c][q], t);
+        acc[tt][c] += bsc[tt] * t;
+      } else {
 #pragma unroll
-      for (int tt = 0; tt < NT; tt++) {
-        if constexpr (FMT == kW8B128) {
-          v4f t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int q = 0; q < 4; q++) t = mfma_bf16(af[tt][q], b[q], t);
-          acc[tt][c] += S32[(size_t)(n0[tt] >> 7) * (K >> 7) + (kk >> 7)] * t;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; q++) acc[tt][c] = mfma_bf16(af[tt][q], b[q], acc[tt][c]);
-        }
+        for (int q = 0; q < 4; q++) acc[tt][c] = mfma_bf16(af[tt][q], b[c][q], acc[tt][c]);
       }
     }
   }
 }
 
+// NT weight tiles of 16 rows times NCG groups of 16 bf16 activation rows over `nsteps`
+// 128-wide K steps, software-pipelined in groups of 4 steps: ring buffers hold the raw
+// weight bytes and the activation fragments of the next 4 steps and the scales of the
+// next group, so every load is issued a group ahead of its use.  Prefetch addresses
+// are clamped to the last step, so the loop has no branches.  Requires nsteps % 4 == 0
+// and 16-byte aligned scale rows.  kb = this lane's first activation K index.
+// acc[tt][c] lane l ends holding C[4*(l/16) + r][l%16]: weight row n0[tt] + 4*(l/16) + r,
+// activation row 16c + l%16.
+template <int FMT, int NT, int NCG>
+__device__ __forceinline__ void tiles_pipe4(const WStream ws[NT], int nsteps, const uint16_t *const xrow[NCG],
+                                            const bool xok[NCG], int kb, int g, v4f acc[NT][NCG]) {
+  constexpr int P = 4;
+  constexpr int PB = NCG == 1 ? 4 : (NCG == 2 ? 2 : 1);  // activation ring depth (16 registers per step and group)
+  RawA ra[P][NT];
+  v4u rb[PB][NCG][4];
+  v4u scg[NT], scn[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; tt++) {
+    scg[tt] = load_scales4<FMT>(ws[tt], 0);
+    scn[tt] = load_scales4<FMT>(ws[tt], nsteps > P ? P : 0);
+  }
+#pragma unroll
+  for (int j = 0; j < P; j++) {
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) load_a<FMT>(ra[j][tt], ws[tt], j);
+  }
+#pragma unroll
+  for (int j = 0; j < PB; j++) {
+#pragma unroll
+    for (int c = 0; c < NCG; c++) load_b(rb[j][c], xrow[c], xok[c], kb + 128 * j);
+  }
+  for (int s = 0; s < nsteps; s += P) {
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+      const int st = s + j;
+      const int sn = st + P < nsteps ? st + P : nsteps - 1;
+      v4u af[NT][4];
+      float bsc[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; tt++) {
+        bsc[tt] = scale_of4<FMT>(scg[tt], j, g);
+        decode_a<FMT>(ra[j][tt], bsc[tt], af[tt]);
+        load_a<FMT>(ra[j][tt], ws[tt], sn);
+      }
+      step_mfma<FMT, NT, NCG>(af, bsc, rb[j % PB], acc);
+      const int snb = st + PB < nsteps ? st + PB : nsteps - 1;
+#pragma unroll
+      for (int c = 0; c < NCG; c++) load_b(rb[j % PB][c], xrow[c], xok[c], kb + 128 * snb);
+    }
+    const int gn = s + 2 * P < nsteps ? s + 2 * P : nsteps - P;
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+      scg[tt] = scn[tt];
+      scn[tt] = load_scales4<FMT>(ws[tt], gn);
+    }
+  }
+}
+
+// Any nsteps and alignment: one step at a time, activations one step ahead.
+template <int FMT, int NT, int NCG>
+__device__ __forceinline__ void tiles_pipe1(const WStream ws[NT], int nsteps, const uint16_t *const xrow[NCG],
+                                            const bool xok[NCG], int kb, int g, v4f acc[NT][NCG]) {
+  for (int st = 0; st < nsteps; st++) {
+    RawA ra[NT];
+    v4u af[NT][4];
+    float bsc[NT];
+    v4u b[NCG][4];
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) load_a<FMT>(ra[tt], ws[tt], st);
+#pragma unroll
+    for (int c = 0; c < NCG; c++) load_b(b[c], xrow[c], xok[c], kb + 128 * st);
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+      bsc[tt] = scale_of1<FMT>(ws[tt], st, g);
+      decode_a<FMT>(ra[tt], bsc[tt], af[tt]);
+    }
+    step_mfma<FMT, NT, NCG>(af, bsc, b, acc);
+  }
+}
+
+// Pipelined path when the step count and scale alignment allow it, else the simple one.
+template <int FMT, int NT, int NCG>
+__device__ __forceinline__ void tiles(const WStream ws[NT], int nsteps, const uint16_t *const xrow[NCG],
+                                      const bool xok[NCG], int kb, int g, v4f acc[NT][NCG]) {
+  bool fast = nsteps % 4 == 0;
+#pragma unroll
+  for (int tt = 0; tt < NT; tt++)
+    fast = fast && (FMT == kW8B128 ? ((uintptr_t)ws[tt].s32 & 15) == 0 : ((uintptr_t)ws[tt].s8 & 15) == 0);
+  if (fast)
+    tiles_pipe4<FMT, NT, NCG>(ws, nsteps, xrow, xok, kb, g, acc);
+  else
+    tiles_pipe1<FMT, NT, NCG>(ws, nsteps, xrow, xok, kb, g, acc);
+}
+
 // One task (16-row tile, K chunk) of a dense linear y = x . W^T with bf16 rows x [M][K]:
-// writes the chunk's partial sums to part[ks][M][N].
-template <int FMT>
-__device__ void linear_task(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32, int N, int K,
-                            int kc, const uint16_t *x, int M, float *part) {
+// writes the chunk's partial sums to part[ks][M][N].  One function per row-group count,
+// so each gets its own register allocation.
+template <int FMT, int NCG>
+__device__ __forceinline__ void linear_task_n(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32,
+                                           int N, int K, int kc, const uint16_t *x, int M, float *part) {
   const int ntile = N >> 4;
   const int ks = t / ntile, nt = t - ks * ntile;
   const int i = lane & 15, g = lane >> 4;
   float *out = part + (size_t)ks * M * N;
-  auto run = [&](auto ncg_c) {
-    constexpr int NCG = decltype(ncg_c)::value;
-    const uint16_t *xrow[NCG];
-    bool xok[NCG];
-    v4f acc[1][NCG];
+  const int k0 = ks * kc;
+  const WStream ws[1] = {wstream<FMT>(W, S8, S32, K, nt * 16 + i, k0, g)};
+  const uint16_t *xrow[NCG];
+  bool xok[NCG];
+  v4f acc[1][NCG];
 #pragma unroll
-    for (int c = 0; c < NCG; c++) {
-      const int m = 16 * c + i;
-      xok[c] = m < M;
-      xrow[c] = x + (size_t)(xok[c] ? m : 0) * K;
-      acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    const int n0[1] = {nt * 16};
-    bf16_tiles<FMT, 1, NCG>(W, S8, S32, K, n0, ks * kc, kc, xrow, xok, acc, lane);
+  for (int c = 0; c < NCG; c++) {
+    const int m = 16 * c + i;
+    xok[c] = m < M;
+    xrow[c] = x + (size_t)(xok[c] ? m : 0) * K;
+    acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  tiles<FMT, 1, NCG>(ws, kc >> 7, xrow, xok, k0 + 32 * g, g, acc);
 #pragma unroll
-    for (int c = 0; c < NCG; c++) {
-      const int m = 16 * c + i;
-      if (m < M) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) out[(size_t)m * N + nt * 16 + 4 * g + r] = acc[0][c][r];
-      }
-    }
-  };
-  const int ncg = (M + 15) >> 4;
-  if (ncg == 1)
-    run(std::integral_constant<int, 1>{});
-  else if (ncg == 2)
-    run(std::integral_constant<int, 2>{});
-  else
-    run(std::integral_constant<int, 3>{});
+  for (int c = 0; c < NCG; c++) {
+    const int m = 16 * c + i;
+    if (m < M) stg(reinterpret_cast<v4f *>(out + (size_t)m * N + nt * 16 + 4 * g), acc[0][c]);
+  }
 }
 
 template <int FMT>
-__device__ void linear_all(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N, int K, int kc,
+__device__ __forceinline__ void linear_task(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32,
+                                            int N, int K, int kc, const uint16_t *x, int M, float *part) {
+  const int ncg = (M + 15) >> 4;
+  if (ncg == 1)
+    linear_task_n<FMT, 1>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+  else if (ncg == 2)
+    linear_task_n<FMT, 2>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+  else
+    linear_task_n<FMT, 3>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+}
+
+template <int FMT>
+__device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N, int K, int kc,
                            const uint16_t *x, int M, float *part) {
   const int T = (N >> 4) * (K / kc);
   for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+}
+
+// ============================================================== block-level helpers
+
+// Sum / max over the block's threads (fixed order: wave results in wave order).
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+}
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+}
+
+// E contiguous float32 values: the sum over nks partial buffers (stride apart).
+template <int E>
+__device__ __forceinline__ void load_sum_f32(const float *p, size_t stride, int nks, float v[E]) {
+  if constexpr (E >= 4) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 a = ld_f4(p + e);
+      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
+    }
+    for (int ks = 1; ks < nks; ks++) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const float4 a = ld_f4(p + ks * stride + e);
+        v[e] += a.x; v[e + 1] += a.y; v[e + 2] += a.z; v[e + 3] += a.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e++) v[e] = ldg(p + e);
+    for (int ks = 1; ks < nks; ks++) {
+#pragma unroll
+      for (int e = 0; e < E; e++) v[e] += ldg(p + ks * stride + e);
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void load_bf16(const uint16_t *p, float v[E]) {
+  if constexpr (E >= 8) {
+#pragma unroll
+    for (int e = 0; e < E; e += 8) {
+      const v4u a = ld16(p + e);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        v[e + 2 * q] = bf16_to_f32(a[q] & 0xFFFFu);
+        v[e + 2 * q + 1] = bf16_to_f32(a[q] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e++) v[e] = bf16_to_f32(ldg(p + e));
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const float v[E]) {
+  if constexpr (E >= 8) {
+#pragma unroll
+    for (int e = 0; e < E; e += 8) {
+      v4u a;
+#pragma unroll
+      for (int q = 0; q < 4; q++) a[q] = f32_to_bf16(v[e + 2 * q]) | (f32_to_bf16(v[e + 2 * q + 1]) << 16);
+      st16(p + e, a);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e++) stg(p + e, (uint16_t)f32_to_bf16(v[e]));
+  }
+}
+
+// MX-quantize E contiguous values per thread (32-blocks span 32/E threads) and keep the
+// dequantized values: v <- e4m3(v / 2^(X-127)) * 2^(X-127).  Inactive threads hold zeros.
+template <int E>
+__device__ __forceinline__ void mx_quant_dequant(float v[E]) {
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; e++) am = fmaxf(am, fabsf(v[e]));
+  if constexpr (E < 32) am = group_max<32 / E>(am);
+  const uint32_t X = mx_e4m3_exponent(am);
+  const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
+#pragma unroll
+  for (int e = 0; e < E; e++) v[e] = e4m3_to_f32(f32_to_e4m3(v[e] * inv)) * sc;
+}
+
+// Elements per thread for a row of n values spread over the block (a power of two).
+__device__ __forceinline__ int row_elems(int n) {
+  int e = 1;
+  while (e * kThreads < n) e <<= 1;
+  return e;
 }
 
 __device__ __forceinline__ float swiglu_clamp(float g, float u, float lim) {
@@ -264,11 +473,22 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float lim) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-// Claim the next task of a device queue (one atomic per wave); returns the task id.
-__device__ __forceinline__ int claim_task(unsigned *ctr, int lane) {
-  unsigned t = 0;
-  if (lane == 0) t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __shfl((int)t, 0, kWave);
-}
+// Device task queue over task ids [0, T): a wave's first task is its global wave id
+// (no atomic), later tasks are claimed past the grid's first round with one atomic
+// per claim on the queue's counter, so a stage start does not serialize every wave on
+// one address.  `ctr` must be zero when the stage begins.
+struct TaskQueue {
+  unsigned *ctr;
+  int nw;
+  int next;  // this wave's next task id
+  __device__ __forceinline__ TaskQueue(unsigned *c, const Ctx &cx) : ctr(c), nw(cx.nw), next(cx.gw) {}
+  __device__ __forceinline__ int take(int lane) {
+    const int t = next;
+    unsigned c = 0;
+    if (lane == 0) c = __hip_atomic_fetch_add(gptr(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    next = nw + __shfl((int)c, 0, kWave);
+    return t;
+  }
+};
 
 }  // namespace dsl

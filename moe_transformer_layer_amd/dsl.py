@@ -51,7 +51,7 @@ class KV(ctypes.Structure):
 
 class Taps(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("attn_out", "hres", "moe_in", "moe_out", "topk_ids", "topk_w",
-                                        "logits")]
+                                        "logits", "layer_ids")]
 
 
 _lib = None
@@ -72,11 +72,13 @@ def lib() -> ctypes.CDLL:
         L.dsl_moe_step.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
         L.dsl_layer_health.argtypes = [c_void_p]
         L.dsl_layer_grid.argtypes = [c_void_p, P(c_int32), P(c_int32)]
+        L.dsl_layer_set_trace.argtypes = [c_void_p, c_int32]
+        L.dsl_layer_read_trace.argtypes = [c_void_p, ctypes.POINTER(ctypes.c_double), c_int32]
         L.dsl_layer_destroy.argtypes = [c_void_p]
         L.dsl_layer_destroy.restype = None
         L.dsl_last_error.restype = ctypes.c_char_p
         for f in ("dsl_layer_build", "dsl_layer_reserve", "dsl_decode_step", "dsl_attn_step", "dsl_moe_step",
-                  "dsl_layer_health", "dsl_layer_grid"):
+                  "dsl_layer_health", "dsl_layer_grid", "dsl_layer_set_trace", "dsl_layer_read_trace"):
             getattr(L, f).restype = c_int32
         _lib = L
     return _lib
@@ -131,6 +133,18 @@ def dsl_layer_grid(h) -> tuple:
     return b.value, t.value
 
 
+def dsl_layer_set_trace(h, on: bool):
+    _check(lib().dsl_layer_set_trace(h, 1 if on else 0))
+
+
+def dsl_layer_read_trace(h, n: int = 256) -> list:
+    buf = (ctypes.c_double * n)()
+    cnt = lib().dsl_layer_read_trace(h, buf, n)
+    if cnt < 0:
+        _check(cnt)
+    return [buf[i] for i in range(cnt)]
+
+
 def dsl_layer_destroy(h):
     lib().dsl_layer_destroy(h)
 
@@ -141,10 +155,35 @@ def dsl_last_error() -> str:
 
 # --------------------------------------------------------------------------- device-side holder
 
-class LayerOnDevice:
-    """Weights, caches and tables of a synthetic case in device memory, and the handle."""
+class DeviceWeights:
+    """One model's layer weights in device memory (torch tensors) and a handle built on them."""
 
-    def __init__(self, case, device="cuda:0", layers: list | None = None):
+    def __init__(self, dims, layers: list, device="cuda:0"):
+        import torch
+        self.dev = torch.device(device)
+        self.dims = dims
+        self.w_dev = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(self.dev) for k, v in lw.items()}
+                      for lw in layers]
+        self.handle = dsl_layer_build(dims_struct(dims), [Weights(**{k: t[k].data_ptr() for k in WEIGHT_FIELDS})
+                                                          for t in self.w_dev])
+
+    def close(self):
+        if self.handle:
+            dsl_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class LayerOnDevice:
+    """Caches, tables and activations of a synthetic case in device memory, with the weights
+    (uploaded here unless a DeviceWeights of the same dims is passed) and the handle."""
+
+    def __init__(self, case, device="cuda:0", weights: DeviceWeights | None = None):
         import torch
         self.torch = torch
         self.dev = torch.device(device)
@@ -152,13 +191,10 @@ class LayerOnDevice:
         d = case.dims
         self.dims = d
         self._keep = []
-        self.w_dev = []
-        wstructs = []
-        for lw in (layers if layers is not None else case.layers):
-            t = {k: self._up(v) for k, v in lw.items()}
-            self.w_dev.append(t)
-            wstructs.append(Weights(**{k: t[k].data_ptr() for k in WEIGHT_FIELDS}))
-        self.handle = dsl_layer_build(dims_struct(d), wstructs)
+        self._owns = weights is None
+        self.weights = weights if weights is not None else DeviceWeights(d, case.layers, device)
+        self.w_dev = self.weights.w_dev
+        self.handle = self.weights.handle
         self.caches = []
         self.kv_structs = []
         if case.kv is not None:
@@ -199,10 +235,12 @@ class LayerOnDevice:
                        moe_out=self.new_bf16(M),
                        ids=torch.zeros((M, self.dims.top_k), dtype=torch.int32, device=self.dev),
                        w=torch.zeros((M, self.dims.top_k), dtype=torch.float32, device=self.dev),
-                       logits=torch.zeros((M, self.dims.n_experts), dtype=torch.float32, device=self.dev))
+                       logits=torch.zeros((M, self.dims.n_experts), dtype=torch.float32, device=self.dev),
+                       layer_ids=torch.zeros((self.dims.n_layers, M, self.dims.top_k), dtype=torch.int32,
+                                             device=self.dev))
             t = Taps(res["attn_out"].data_ptr(), res["hres"].data_ptr(), res["moe_in"].data_ptr(),
                      res["moe_out"].data_ptr(), res["ids"].data_ptr(), res["w"].data_ptr(),
-                     res["logits"].data_ptr())
+                     res["logits"].data_ptr(), res["layer_ids"].data_ptr())
         dsl_decode_step(self.handle, x.data_ptr(), M, self.kv_structs, self.positions.data_ptr(),
                         out.data_ptr(), t, self.stream())
         torch.cuda.synchronize(self.dev)
@@ -243,12 +281,6 @@ class LayerOnDevice:
         return out
 
     def close(self):
-        if self.handle:
-            dsl_layer_destroy(self.handle)
-            self.handle = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        if self.handle and self._owns:
+            self.weights.close()
+        self.handle = None

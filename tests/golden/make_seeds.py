@@ -1,0 +1,68 @@
+"""Find, for each full-size parity case, the first input seed whose oracle router logits
+keep every live row's top-k gap (k-th minus (k+1)-th largest logit) at or above 1e-3,
+in every layer, and store it in seeds.json next to this script.
+
+Calls only the input generator and the oracle.  Run: python tests/golden/make_seeds.py
+[key ...]  (about ten minutes on one core for all keys)."""
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.dirname(HERE))
+
+import numpy as np  # noqa: E402
+
+from moe_transformer_layer_amd import synth  # noqa: E402
+from oracle import layer as OL  # noqa: E402
+
+GAP_MIN = 1e-3
+OUT = os.path.join(HERE, "seeds.json")
+
+# key -> (config name, weights seed, make_case keyword arguments, kind)
+CASES = {
+    "moe6": ("moe6", 5, dict(), "moe"),
+    "layer48_m48": ("layer48", 7, dict(M=48), "decode"),
+    "layer48_m6": ("layer48", 7, dict(M=6), "decode"),
+    **{f"draft_m{m}": ("draft", 11, dict(M=m), "decode") for m in (1, 6, 12, 24, 36, 48)},
+}
+
+
+def gap_of(case, kind):
+    d = case.dims
+    if kind == "moe":
+        r = OL.moe_step(d, case.layers[0], case.x)
+        return float(OL.topk_gap(r["logits"], d.top_k).min()), [r["n_distinct"]]
+    caches = [c.copy() for c in case.kv.cache]
+    r = OL.decode_step(d, case.layers, case.x, case.kv, caches)
+    live = case.kv.positions >= 0
+    g = min(float(OL.topk_gap(x["logits"], d.top_k)[live].min()) for x in r["layers"])
+    return g, [x["n_distinct"] for x in r["layers"]]
+
+
+def main(keys):
+    seeds = json.load(open(OUT)) if os.path.exists(OUT) else {}
+    weights = {}
+    for key in keys:
+        name, wseed, kw, kind = CASES[key]
+        if (name, wseed) not in weights:
+            weights.clear()
+            weights[(name, wseed)] = synth.make_weights(name, wseed)
+        layers = weights[(name, wseed)]
+        for s in range(1000):
+            t = time.time()
+            case = synth.make_case(name, s, layers=layers, **kw)
+            g, nd = gap_of(case, kind)
+            print(f"{key} seed {s}: min gap {g:.3g} distinct {nd} ({time.time() - t:.1f}s)", flush=True)
+            if g >= GAP_MIN:
+                seeds[key] = dict(config=name, weights_seed=wseed, seed=s, min_gap=g, n_distinct=nd, **kw)
+                break
+        with open(OUT, "w") as f:
+            json.dump(seeds, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:] or list(CASES))

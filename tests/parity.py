@@ -35,11 +35,18 @@ def check_bf16(name: str, got, want, report: dict | None = None):
     g, w = bf16_value(got), bf16_value(want)
     assert g.shape == w.shape, (name, g.shape, w.shape)
     assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
-    maxabs = float(np.abs(g - w).max()) if g.size else 0.0
+    err = np.abs(g - w)
+    maxabs = float(err.max()) if g.size else 0.0
     c = cos(g, w)
     if report is not None:
         report[name] = (maxabs, c)
-    assert maxabs <= ATOL and c >= COS_MIN, f"{name}: max-abs {maxabs:.4g} (bar {ATOL}), cos {c:.7f} (bar {COS_MIN})"
+    if not (maxabs <= ATOL and c >= COS_MIN):
+        rows = err.reshape(err.shape[0], -1).max(axis=1)
+        worst = np.argsort(-rows)[:4]
+        where = np.unravel_index(int(err.argmax()), err.shape)
+        detail = ", ".join(f"row {int(r)}: {rows[r]:.3g}" for r in worst)
+        raise AssertionError(f"{name}: max-abs {maxabs:.4g} (bar {ATOL}) at {where} got {g[where]:.5g} want "
+                             f"{w[where]:.5g}, cos {c:.7f} (bar {COS_MIN}); worst rows {detail}")
     return maxabs, c
 
 
