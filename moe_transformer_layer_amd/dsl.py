@@ -9,6 +9,7 @@ library every call raises.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from ctypes import c_float, c_int32, c_int64, c_void_p
 
@@ -166,6 +167,16 @@ class DeviceWeights:
                       for lw in layers]
         self.handle = dsl_layer_build(dims_struct(dims), [Weights(**{k: t[k].data_ptr() for k in WEIGHT_FIELDS})
                                                           for t in self.w_dev])
+
+    def single(self, l: int) -> "DeviceWeights":
+        """A one-layer handle on layer l's tensors (shared, not copied)."""
+        sub = DeviceWeights.__new__(DeviceWeights)
+        sub.dev, sub.dims = self.dev, dataclasses.replace(self.dims, n_layers=1)
+        sub.w_dev = [self.w_dev[l]]
+        sub._parent = self
+        sub.handle = dsl_layer_build(dims_struct(sub.dims), [Weights(**{k: self.w_dev[l][k].data_ptr()
+                                                                         for k in WEIGHT_FIELDS})])
+        return sub
 
     def close(self):
         if self.handle:

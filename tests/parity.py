@@ -31,28 +31,44 @@ def cos(a, b) -> float:
     return float(a @ b / (na * nb))
 
 
-def check_bf16(name: str, got, want, report: dict | None = None):
+def bf16_ulp(v) -> np.ndarray:
+    """Spacing of bfloat16 at |v| (8 significant bits), 2^-133 at zero."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def check_bf16(name: str, got, want, report: dict | None = None, ulps: float | None = None,
+               atol: float = ATOL):
+    """max-abs <= atol and cosine >= COS_MIN; with `ulps`, each element may instead be
+    within that many bfloat16 steps of the oracle's value (for intermediates that a
+    one-step flip upstream moves by more than one step)."""
     g, w = bf16_value(got), bf16_value(want)
     assert g.shape == w.shape, (name, g.shape, w.shape)
     assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
     err = np.abs(g - w)
+    bar = np.maximum(atol, ulps * bf16_ulp(w)) if ulps else np.full(err.shape, atol)
+    over = err / bar
     maxabs = float(err.max()) if g.size else 0.0
     c = cos(g, w)
     if report is not None:
         report[name] = (maxabs, c)
-    if not (maxabs <= ATOL and c >= COS_MIN):
-        rows = err.reshape(err.shape[0], -1).max(axis=1)
+    if not ((over <= 1).all() and c >= COS_MIN):
+        rows = over.reshape(over.shape[0], -1).max(axis=1)
         worst = np.argsort(-rows)[:4]
-        where = np.unravel_index(int(err.argmax()), err.shape)
-        detail = ", ".join(f"row {int(r)}: {rows[r]:.3g}" for r in worst)
-        raise AssertionError(f"{name}: max-abs {maxabs:.4g} (bar {ATOL}) at {where} got {g[where]:.5g} want "
-                             f"{w[where]:.5g}, cos {c:.7f} (bar {COS_MIN}); worst rows {detail}")
+        where = np.unravel_index(int(over.argmax()), err.shape)
+        detail = ", ".join(f"row {int(r)}: {rows[r]:.3g} of the bar" for r in worst)
+        raise AssertionError(f"{name}: error {err[where]:.4g} (bar {bar[where]:.3g}) at {where} got {g[where]:.5g} "
+                             f"want {w[where]:.5g}, cos {c:.7f} (bar {COS_MIN}); worst rows {detail}")
     return maxabs, c
 
 
-def check_routing(got_ids, got_w, want_ids, want_w, live, w_tol: float, report: dict | None = None):
+def check_routing(got_ids, got_w, want_ids, want_w, live, w_tol, report: dict | None = None):
+    """Ids equal as sets per live row; weights per id within w_tol (a scalar or one bar
+    per row); each live row's weights sum to 1; pad rows carry ids -1 and weight 0."""
     M, k = want_ids.shape
-    worst = 0.0
+    tol = np.broadcast_to(np.asarray(w_tol, dtype=np.float64), (M,))
+    worst, worst_frac = 0.0, 0.0
     for m in range(M):
         if not live[m]:
             assert (got_ids[m] == -1).all() and (got_w[m] == 0).all(), f"pad row {m} routed"
@@ -62,10 +78,29 @@ def check_routing(got_ids, got_w, want_ids, want_w, live, w_tol: float, report: 
             f"row {m}: ids {sorted(got_ids[m].tolist())} vs oracle {sorted(want_ids[m].tolist())}"
         d = float(np.abs(got_w[m][gs] - want_w[m][ws]).max())
         worst = max(worst, d)
+        worst_frac = max(worst_frac, d / tol[m])
         assert abs(float(got_w[m].sum()) - 1.0) < 1e-5
     if report is not None:
         report["router_w_maxdiff"] = worst
-    assert worst <= w_tol, f"router weights differ by {worst:.3g} (bar {w_tol})"
+    assert worst_frac <= 1.0, f"router weights differ by up to {worst_frac:.3g} of their bar (max {worst:.3g})"
+
+
+def check_logits(got_l, want_l, got_u, want_u, w_router, live, report: dict | None = None,
+                 tol: float = 1e-4):
+    """The logits are a float32 linear map of moe_in, so the GPU's deviation from the
+    oracle must be accounted for by its moe_in deviation:
+    |dl_e| <= sum_j |W_ej| |du_j| + tol (tol covers float32 summation over the row).
+    Returns the per-row max |dl|, from which the router weights' bar follows."""
+    du = np.abs(bf16_value(got_u).astype(np.float64) - bf16_value(want_u))
+    bound = du @ np.abs(np.asarray(w_router, dtype=np.float64)).T + tol
+    dl = np.abs(np.asarray(got_l, dtype=np.float64) - want_l)
+    dl[~live] = 0
+    ratio = float((dl / bound)[live].max()) if live.any() else 0.0
+    if report is not None:
+        report["logits_maxdiff"] = float(dl.max())
+        report["logits_vs_bound"] = ratio
+    assert ratio <= 1.0, f"router logits deviate by {ratio:.3g} of what moe_in's deviation explains"
+    return dl.max(axis=1)
 
 
 def _code_index(c):
@@ -73,28 +108,69 @@ def _code_index(c):
     return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
 
 
+def _record_values(c, D):
+    codes = c[:, :D]
+    from oracle.formats import e4m3_value
+    sc = c[:, D:D + 4].copy().view(np.float32).astype(np.float64)
+    return e4m3_value(codes) * sc
+
+
+REC_SCALE_REL = 1e-5
+REC_SCALE_REL_FLIP = 4e-3
+REC_LATENT_SHIFT = 1e-2
+
+
 def check_records(d, got_cache, want_cache, before, report: dict | None = None):
-    """Records the step wrote: e4m3 codes within one step (>= 99.9% identical), scales
-    within 1e-5 relative, pad bytes zero; every other byte unchanged."""
+    """Records the step wrote, against the oracle's; every other byte unchanged.
+
+    Strict bar per record: scale within REC_SCALE_REL relative, e4m3 codes within one
+    step, and >= 99.9% of codes over the strict records identical (the float32 kv
+    latents differ by summation order, so a quotient near a rounding midpoint may round
+    either way).  A record may miss the strict bar when its row's input activation had
+    one MXFP8 code rounded the other way: both sides quantize float32 norm outputs that
+    differ in the last place, and one e4m3 step of an activation (at most 0.25 for
+    values below 4) moves every kv latent element of that row by up to one weight
+    (|w| <= 0.023) times that step, i.e. ~6e-3 (below REC_LATENT_SHIFT after the kv
+    norm), a scale change of up to ~4e-3 relative, and a shift of many codes by a step
+    or, for elements near zero, across zero.  Such records (at most max(1, n/16) of n)
+    must keep the scale within REC_SCALE_REL_FLIP and each dequantized value within one
+    e4m3 step of the oracle's code, plus the scale change, plus REC_LATENT_SHIFT."""
     D = d.head_dim
     changed = (want_cache != before).any(axis=2) | (got_cache != before).any(axis=2)
     assert np.array_equal(got_cache[~changed], before[~changed])
     g, w = got_cache[changed], want_cache[changed]
     if g.size == 0:
         return
+    assert not g[:, D + 4:].any(), "KV record pad bytes not zero"
     gi, wi = _code_index(g[:, :D]), _code_index(w[:, :D])
     step = np.abs(gi - wi)
-    same = float((step == 0).mean())
     gs = g[:, D:D + 4].copy().view(np.float32).ravel()
     ws = w[:, D:D + 4].copy().view(np.float32).ravel()
-    rel = float(np.max(np.abs(gs - ws) / np.maximum(np.abs(ws), 1e-30)))
+    rel = np.abs(gs.astype(np.float64) - ws) / np.maximum(np.abs(ws), 1e-30)
+    strict = (rel <= REC_SCALE_REL) & (step.max(axis=1) <= 1)
+    loose = ~strict
+    same = float((step[strict] == 0).mean()) if strict.any() else 1.0
+    dv = np.abs(_record_values(g[loose], D) - _record_values(w[loose], D))
+    if loose.any():
+        from oracle.formats import e4m3_value
+        q = np.abs(e4m3_value(w[loose][:, :D]))
+        ws_l = np.abs(ws[loose]).astype(np.float64)[:, None]
+        e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+        allow = ws_l * np.ldexp(1.0, (e - 3).astype(np.int64)) + REC_SCALE_REL_FLIP * q * ws_l + REC_LATENT_SHIFT
+        dv_ratio = float((dv / allow).max())
     if report is not None:
         report["kv_codes_identical"] = same
-        report["kv_scale_rel"] = rel
-    assert step.max() <= 1, f"KV code off by {step.max()} steps"
+        report["kv_scale_rel"] = float(rel[strict].max()) if strict.any() else 0.0
+        report["kv_records_flipped"] = int(loose.sum())
+        if loose.any():
+            report["kv_flipped_scale_rel"] = float(rel[loose].max())
+            report["kv_flipped_value_maxabs"] = float(dv.max())
+    n = len(g)
+    assert loose.sum() <= max(1, n // 16), f"{int(loose.sum())} of {n} KV records miss the strict bar"
     assert same >= 0.999, f"only {same:.5f} of KV codes identical"
-    assert rel <= 1e-5, f"KV scale relative difference {rel:.3g}"
-    assert not g[:, D + 4:].any(), "KV record pad bytes not zero"
+    if loose.any():
+        assert rel[loose].max() <= REC_SCALE_REL_FLIP, f"KV scale relative difference {rel[loose].max():.3g}"
+        assert dv_ratio <= 1.0, f"KV record values differ by up to {dv_ratio:.3g} of their bar"
 
 
 def min_gap(d, res_layers: list, live) -> float:
@@ -136,5 +212,5 @@ def decode_live(case):
     return case.kv.positions >= 0
 
 
-__all__ = ["synth", "check_bf16", "check_routing", "check_records", "gap_seed", "oracle_decode", "cos",
+__all__ = ["synth", "check_bf16", "check_routing", "check_logits", "bf16_ulp", "check_records", "gap_seed", "oracle_decode", "cos",
            "decode_live", "min_gap", "ATOL", "COS_MIN", "GAP_MIN"]

@@ -8,19 +8,49 @@ make_seeds.py with the oracle alone); each test re-checks the top-k gap rule.
   full layer, top-6, M = 48 and M = 6           (layer48)
   three draft layers, 192-wide index rows, top-3, M in {1, 6, 12, 24, 36, 48}, one
   handle for all widths (each width gets its own scratch)  (draft)
+
+Tolerances beyond the common bf16 bar, and why:
+
+* moe_in = bf16(RMSNorm(hres)): both sides see the same layer input, but
+  hres = bf16(x + attention) is rounded from float32 sums taken in a different order,
+  so now and then an element of hres lands one bf16 step away; RMSNorm scales that step
+  by gamma / rms (up to ~1.2 here), which can round to two steps of moe_in.  moe_in may
+  differ by two bf16 steps per element; the layer output keeps the common bar.
+* Router logits: an f32 linear map of moe_in, so their deviation must be what moe_in's
+  deviation explains, |dl_e| <= sum_j |W_ej| |du_j| + 1e-4 (the 1e-4 covers float32
+  summation over 4096 terms).
+* Router weights: w_i = softmax over the selected logits, so
+  dw_i = w_i (dl_i - sum_j w_j dl_j) and |dw_i| <= 2 w_i (1 - w_i) max|dl|
+  <= max|dl| / 2 over the row's selected experts (+1e-6).  The MoE stage alone has
+  identical inputs on both sides and keeps 1e-5.
+* Chained draft layers: layer l >= 1 is fed each side's own layer l-1 output, which
+  differ by that layer's rounding.  So each layer is checked on its own with the
+  oracle's input for that layer, at the bars above; the fused launch is checked bit for
+  bit against its single-layer launches composed; and against the oracle's chain, whose
+  output error is the sum of the per-layer errors carried by the residual stream, at
+  max-abs <= n_layers x 2e-2 and cosine >= 0.9995, on the rows whose routing matched in
+  every layer.  Through 4096 router entries of sigma 0.02 the carried error (rms about
+  2e-3) moves a logit by up to about 4 x 0.02 x 64 x 2e-3 = 1e-2 = G_DRIFT, more than
+  the 1e-3 gap the seeds guarantee, so a divergence in layers >= 1 is allowed where the
+  oracle's gap there is below G_DRIFT, and the GPU's choice must then be a top-k within
+  G_DRIFT of the oracle's logits.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
 from moe_transformer_layer_amd import synth
 from oracle import layer as OL
-from parity import (GAP_MIN, check_bf16, check_records, check_routing, decode_live, load_seeds, min_gap,
-                    oracle_decode)
+from oracle.formats import bf16_value
+from parity import (ATOL, COS_MIN, GAP_MIN, check_bf16, check_logits, check_records, check_routing, cos,
+                    decode_live, load_seeds, min_gap, oracle_decode)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 W_TOL_MOE = 1e-5
-W_TOL_LAYER = 1e-4
+MOE_IN_ULPS = 2
+G_DRIFT = 1e-2
 SEEDS = load_seeds()
 
 
@@ -54,7 +84,36 @@ def _seeded(key):
     return SEEDS[key]
 
 
-def _run_decode(dsl, name, key):
+class Errors:
+    def __init__(self):
+        self.msgs, self.rep = [], {}
+
+    def attempt(self, f, *a, rep=None, **kw):
+        try:
+            return f(*a, self.rep if rep is None else rep, **kw)
+        except AssertionError as e:
+            self.msgs.append(str(e))
+
+    def raise_any(self, key):
+        _say(f"{key}: {self.rep}")
+        assert not self.msgs, f"{key}: " + " | ".join(self.msgs)
+
+
+def _check_layer(er: Errors, d, lw, got, want, live, got_cache, want_cache, before, tag="L0"):
+    rep = er.rep.setdefault(tag, {})
+    for k in ("attn_out", "hres", "moe_out", "out"):
+        er.attempt(check_bf16, f"{tag}.{k}", got[k], want[k], rep=rep)
+    er.attempt(check_bf16, f"{tag}.moe_in", got["moe_in"], want["moe_in"], rep=rep, ulps=MOE_IN_ULPS)
+    dl = er.attempt(check_logits, got["logits"], want["logits"], got["moe_in"], want["moe_in"], lw["w_router"],
+                    live, rep=rep)
+    if dl is not None:
+        sel = np.take_along_axis(np.abs(got["logits"].astype(np.float64) - want["logits"]),
+                                 np.maximum(want["ids"], 0), axis=1).max(axis=1)
+        er.attempt(check_routing, got["ids"], got["w"], want["ids"], want["w"], live, sel / 2 + 1e-6, rep=rep)
+    er.attempt(check_records, d, got_cache, want_cache, before, rep=rep)
+
+
+def _case_and_oracle(dsl, name, key):
     sd = _seeded(key)
     layers, dw = _device_weights(dsl, name, sd["weights_seed"])
     case = synth.make_case(name, sd["seed"], M=sd["M"], layers=layers)
@@ -62,26 +121,101 @@ def _run_decode(dsl, name, key):
     live = decode_live(case)
     g = min_gap(case.dims, res["layers"], live)
     assert g >= GAP_MIN, f"{key}: top-k gap {g} below {GAP_MIN}"
+    return case, res, caches, live, dw
+
+
+def _layer_case(case, l, x_bits):
+    """Layer l of a chained case as a one-layer case on input x_bits."""
+    kv = dataclasses.replace(case.kv, cache=[case.kv.cache[l]])
+    return dataclasses.replace(case, dims=dataclasses.replace(case.dims, n_layers=1), layers=[case.layers[l]],
+                               kv=kv, x=x_bits)
+
+
+def _run_decode(dsl, name, key):
+    case, res, caches, live, dw = _case_and_oracle(dsl, name, key)
     dev = dsl.LayerOnDevice(case, weights=dw)
     _say(f"{key}: decode M={case.M} layers={case.dims.n_layers}")
     got = dev.decode(case.x)
     got_caches = dev.caches_host()
     dev.close()
-    rep, errors = {}, []
+    er = Errors()
+    _check_layer(er, case.dims, case.layers[0], got, res, live, got_caches[0], caches[0], case.kv.cache[0])
+    er.raise_any(key)
 
-    def attempt(f, *a):
-        try:
-            f(*a)
-        except AssertionError as e:
-            errors.append(str(e))
 
-    for k in ("attn_out", "hres", "moe_in", "moe_out", "out"):
-        attempt(check_bf16, k, got[k], res[k], rep)
-    attempt(check_routing, got["ids"], got["w"], res["ids"], res["w"], live, W_TOL_LAYER, rep)
-    for l in range(case.dims.n_layers):
-        attempt(check_records, case.dims, got_caches[l], caches[l], case.kv.cache[l], rep)
-    _say(f"{key}: {rep}")
-    assert not errors, f"{key}: " + " | ".join(errors)
+def _run_chain(dsl, name, key):
+    case, res, caches, live, dw = _case_and_oracle(dsl, name, key)
+    d, L, M = case.dims, case.dims.n_layers, case.M
+    er = Errors()
+
+    # 1. every layer on the oracle's input for that layer
+    x_in = case.x
+    singles = [dw.single(l) for l in range(L)]
+    for l in range(L):
+        lc = _layer_case(case, l, x_in)
+        dev = dsl.LayerOnDevice(lc, weights=singles[l])
+        _say(f"{key}: layer {l} alone on the oracle's input, M={M}")
+        got = dev.decode(x_in)
+        gc = dev.caches_host()[0]
+        dev.close()
+        _check_layer(er, d, case.layers[l], got, res["layers"][l], live, gc, caches[l], case.kv.cache[l],
+                     tag=f"L{l}")
+        x_in = res["layers"][l]["out"]
+
+    # 2. the fused launch against its single-layer launches composed
+    dev = dsl.LayerOnDevice(case, weights=dw)
+    _say(f"{key}: fused {L}-layer decode M={M}")
+    chain = dev.decode(case.x)
+    chain_caches = dev.caches_host()
+    dev.close()
+    x_in = case.x
+    for l in range(L):
+        lc = _layer_case(case, l, x_in)
+        dev = dsl.LayerOnDevice(lc, weights=singles[l])
+        one = dev.decode(x_in)
+        oc = dev.caches_host()[0]
+        dev.close()
+        if not np.array_equal(chain["layer_ids"][l], one["ids"]):
+            er.msgs.append(f"fused layer {l} ids differ from the single-layer launch")
+        if not np.array_equal(chain_caches[l], oc):
+            er.msgs.append(f"fused layer {l} KV records differ from the single-layer launch")
+        x_in = one["out"]
+    for k in ("out", "attn_out", "hres", "moe_in", "moe_out", "w", "logits"):
+        if not np.array_equal(chain[k], one[k]):
+            er.msgs.append(f"fused last-layer {k} differs from the composed single-layer launches")
+    for s in singles:
+        s.close()
+
+    # 3. the fused chain against the oracle's chain
+    ok = live.copy()
+    for l in range(L):
+        want = res["layers"][l]
+        gap = OL.topk_gap(want["logits"], d.top_k)
+        for m in np.flatnonzero(live):
+            gi, wi = sorted(chain["layer_ids"][l][m].tolist()), sorted(want["ids"][m].tolist())
+            if gi == wi:
+                continue
+            if l == 0 or not ok[m] or gap[m] >= G_DRIFT:
+                if ok[m]:
+                    er.msgs.append(f"layer {l} row {m}: ids {gi} vs oracle {wi}, oracle gap {gap[m]:.3g}")
+                ok[m] = False
+                continue
+            kth = np.sort(want["logits"][m])[-d.top_k]
+            if not (want["logits"][m][gi] >= kth - G_DRIFT).all():
+                er.msgs.append(f"layer {l} row {m}: ids {gi} are not a top-{d.top_k} within {G_DRIFT}")
+            ok[m] = False
+    er.rep["rows_diverged"] = int((live & ~ok).sum())
+    if (live & ~ok).sum() > max(1, M // 8):
+        er.msgs.append(f"{(live & ~ok).sum()} of {live.sum()} rows diverged")
+    for k in ("out", "hres", "moe_out"):
+        g, w = bf16_value(chain[k][ok]), bf16_value(res[k][ok])
+        e = float(np.abs(g - w).max()) if g.size else 0.0
+        c = cos(g, w)
+        er.rep[f"chain.{k}"] = (e, c)
+        if not (e <= L * ATOL and c >= COS_MIN):
+            er.msgs.append(f"chain {k}: max-abs {e:.4g} (bar {L * ATOL}), cos {c:.7f} on rows whose routing "
+                           f"matched")
+    er.raise_any(key)
 
 
 def test_moe_stage_m6_top3(dsl):
@@ -127,4 +261,4 @@ def test_full_layer_m6_top6(dsl):
 
 @pytest.mark.parametrize("M", [1, 6, 12, 24, 36, 48])
 def test_draft_three_layers(dsl, M):
-    _run_decode(dsl, "draft", f"draft_m{M}")
+    _run_chain(dsl, "draft", f"draft_m{M}")
