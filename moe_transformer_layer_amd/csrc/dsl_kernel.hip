@@ -437,32 +437,46 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
 
 // Top-k of every live row (ties to the lower id, descending order, weights = softmax of
 // the selected logits), then the distinct-expert list and the (row, slot) -> pair map
-// ordered by expert id.  Every block builds the same routing in its own LDS.
+// ordered by expert id, then by row.  Every block builds the same routing in its own LDS.
+constexpr int kRowsPerWave = (DSL_MAX_ROWS + kWavesPerBlock - 1) / kWavesPerBlock;
+
 __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
-  const int k = p.k, E = p.E;
+  const int k = p.k, E = p.E, M = p.M, lane = cx.lane;
   for (int e = threadIdx.x; e < 128; e += kThreads) R.cnt[e] = 0;
+  // every logit load of this wave's rows in flight at once
+  float l0[kRowsPerWave], l1[kRowsPerWave];
+  bool live[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r++) {
+    const int m = cx.wave + r * kWavesPerBlock;
+    const int mc = m < M ? m : M - 1;
+    live[r] = m < M && (all_live || ldg(p.pos + mc) >= 0);
+    const float *lg = p.s.logits + (size_t)mc * E;
+    l0[r] = lane < E ? ldg(lg + lane) : -INFINITY;
+    l1[r] = lane + 64 < E ? ldg(lg + lane + 64) : -INFINITY;
+  }
   __syncthreads();
-  for (int m = cx.wave; m < p.M; m += kWavesPerBlock) {
-    const bool live = all_live || ldg(p.pos + m) >= 0;
-    if (!live) {
-      if (cx.lane < k) {
-        R.ids[m * k + cx.lane] = -1;
-        R.w[m * k + cx.lane] = 0.f;
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r++) {
+    const int m = cx.wave + r * kWavesPerBlock;
+    if (m >= M) break;
+    if (!live[r]) {
+      if (lane < k) {
+        R.ids[m * k + lane] = -1;
+        R.w[m * k + lane] = 0.f;
       }
       continue;
     }
-    const float *lg = p.s.logits + (size_t)m * E;
-    float l0 = cx.lane < E ? ldg(lg + cx.lane) : -INFINITY;
-    float l1 = cx.lane + 64 < E ? ldg(lg + cx.lane + 64) : -INFINITY;
+    float a0 = l0[r], a1 = l1[r];
     int myid = -1;
     float myval = -INFINITY;
     for (int j = 0; j < k; j++) {
       float bv;
       int bi;
-      if (l0 >= l1) {
-        bv = l0; bi = cx.lane;
+      if (a0 >= a1) {
+        bv = a0; bi = lane;
       } else {
-        bv = l1; bi = cx.lane + 64;
+        bv = a1; bi = lane + 64;
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
@@ -472,45 +486,57 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
           bv = ov; bi = oi;
         }
       }
-      if (cx.lane == j) {
+      if (lane == j) {
         myid = bi; myval = bv;
       }
-      if (bi == cx.lane) l0 = -INFINITY;
-      if (bi == cx.lane + 64) l1 = -INFINITY;
+      if (bi == lane) a0 = -INFINITY;
+      if (bi == lane + 64) a1 = -INFINITY;
     }
     const float top = __shfl(myval, 0, kWave);
-    const float ev = cx.lane < k ? expf(myval - top) : 0.f;
+    const float ev = lane < k ? expf(myval - top) : 0.f;
     const float sum = wave_sum(ev);
-    if (cx.lane < k) {
-      R.ids[m * k + cx.lane] = myid;
-      R.w[m * k + cx.lane] = ev / sum;
+    if (lane < k) {
+      R.ids[m * k + lane] = myid;
+      R.w[m * k + lane] = ev / sum;
       atomicAdd(&R.cnt[myid], 1);
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0, nd = 0;
-    for (int e = 0; e < E; e++) {
-      R.start[e] = acc;
-      if (R.cnt[e]) {
-        R.list[nd++] = e;
-        acc += R.cnt[e];
+  // starts (exclusive scan of the counts in expert order) and the compacted expert list:
+  // wave 0, experts lane and lane + 64
+  if (cx.wave == 0) {
+    const int c0 = R.cnt[lane], c1 = R.cnt[lane + 64];
+    int s0 = c0, s1 = c1;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t0 = __shfl_up(s0, o, kWave), t1 = __shfl_up(s1, o, kWave);
+      if (lane >= o) {
+        s0 += t0; s1 += t1;
       }
     }
-    R.nd = nd;
+    const int tot0 = __shfl(s0, kWave - 1, kWave);
+    R.start[lane] = s0 - c0;
+    R.start[lane + 64] = tot0 + s1 - c1;
+    const unsigned long long b0 = __ballot(c0 > 0), b1 = __ballot(c1 > 0);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int n0 = __popcll(b0);
+    if (c0 > 0) R.list[__popcll(b0 & below)] = lane;
+    if (c1 > 0) R.list[n0 + __popcll(b1 & below)] = lane + 64;
+    if (lane == 0) R.nd = n0 + __popcll(b1);
   }
   __syncthreads();
-  const int P = p.M * k;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    if (!R.cnt[e]) continue;
-    int r = 0;
-    for (int t = 0; t < P; t++) {
-      if (R.ids[t] == e) {
-        R.pair[t] = R.start[e] + r;
-        R.pair_row[R.start[e] + r] = t / k;
-        r++;
-      }
-    }
+  // rank of pair t among the earlier pairs of its expert (ids of one row are distinct, so
+  // earlier pairs are earlier rows)
+  const int P = M * k;
+  for (int t = threadIdx.x; t < P; t += kThreads) {
+    const int id = R.ids[t];
+    if (id < 0) continue;
+    const int m = t / k;
+    int rank = 0;
+    for (int u = 0; u < m * k; u++) rank += R.ids[u] == id;
+    const int slot = R.start[id] + rank;
+    R.pair[t] = slot;
+    R.pair_row[slot] = m;
   }
   __syncthreads();
 }
@@ -595,13 +621,10 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
 
 // Routed gate/up tasks (selected expert, 16-row tile of gate and of up) from the queue
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
-                                  const uint16_t *u, unsigned *ctr) {
+                                  const uint16_t *u) {
   const int tiles_n = p.I >> 4;
   const int T = R.nd * tiles_n;
-  TaskQueue tq(ctr, cx);
-  for (;;) {
-    const int t = tq.take(cx.lane);
-    if (t >= T) break;
+  for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
@@ -615,16 +638,13 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
 }
 
 // Shared down partials (static split), then routed down tasks from the queue
-__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R, unsigned *ctr) {
+__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
   for (int t = cx.gw; t < TS; t += cx.nw)
     linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
   const int tiles_n = p.h >> 4;
   const int T = R.nd * tiles_n;
-  TaskQueue tq(ctr, cx);
-  for (;;) {
-    const int t = tq.take(cx.lane);
-    if (t >= T) break;
+  for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
@@ -662,21 +682,51 @@ __device__ __forceinline__ void st_combine_out(const Params &p, const Routing &R
 
 // ============================================================== the persistent launch
 
-// One layer's weight descriptors from device memory (global loads of its pointer words)
-__device__ __forceinline__ dsl_weights load_weights(const dsl_weights *src) {
-  static_assert(sizeof(dsl_weights) % 8 == 0, "descriptor size");
-  dsl_weights w;
-  const uint64_t *s = reinterpret_cast<const uint64_t *>(src);
-  uint64_t *d = reinterpret_cast<uint64_t *>(&w);
+// Launch parameters are read per stage through the constant address space: the empty
+// asm makes each stage's pointer opaque, so its scalar loads are not merged with (and
+// kept live from) another stage's, and nothing uniform stays in registers across the
+// launch.  The descriptors (the kernel argument, the weight table) are read-only for
+// the whole launch.
+typedef const Params __attribute__((address_space(4))) KParams;
+typedef const dsl_weights __attribute__((address_space(4))) KWeights;
+
+__device__ __forceinline__ KParams *kparams() {
+  KParams *kp = (KParams *)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return kp;
+}
+
+// a descriptor copied in 64-bit words by scalar loads
+template <typename T>
+__device__ __forceinline__ T kload(const __attribute__((address_space(4))) T *src) {
+  static_assert(sizeof(T) % 8 == 0, "descriptor size");
+  T v;
+  const __attribute__((address_space(4))) uint64_t *s = (const __attribute__((address_space(4))) uint64_t *)src;
+  uint64_t *d = reinterpret_cast<uint64_t *>(&v);
 #pragma unroll
-  for (int i = 0; i < (int)(sizeof(dsl_weights) / 8); i++) d[i] = ldg(s + i);
-  return w;
+  for (int i = 0; i < (int)(sizeof(T) / 8); i++) d[i] = s[i];
+  return v;
+}
+
+struct StageArgs {
+  Params p;
+  dsl_weights w;
+  dsl_kv kv;
+};
+
+__device__ __forceinline__ StageArgs stage_args(int l) {
+  KParams *kp = kparams();
+  StageArgs a;
+  a.p = kload(kp);
+  a.w = kload((KWeights *)kp->w + l);
+  a.kv = kload(&kp->kv[l]);
+  return a;
 }
 
 // Block 0 stamps the device wall clock at the start, after every grid barrier and at
 // the end of a launch when tracing is on (one entry per stage boundary).
 struct Tracer {
-  unsigned long long *buf;
+  unsigned long long *buf = nullptr;
   int n = 0;
   __device__ __forceinline__ void mark() {
     if (buf && blockIdx.x == 0 && threadIdx.x == 0) buf[n] = wall_clock64();
@@ -684,124 +734,183 @@ struct Tracer {
   }
 };
 
-__global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p) {
+#define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
+  const dsl_kv &kv = A_.kv; (void)p; (void)w; (void)kv
+
+__global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
+  (void)p_arg;
   __shared__ Routing R;
   __shared__ float red[16];
   const Ctx cx = make_ctx();
-  SyncWords *sw = p.sync;
   const unsigned nb = gridDim.x;
+  int mode, n_layers;
+  SyncWords *sw;
+  Tracer tr;
+  {
+    KParams *kp = kparams();
+    mode = kp->mode;
+    n_layers = kp->n_layers;
+    sw = kp->sync;
+    tr.buf = kp->trace;
+  }
   if (blockIdx.x == 0 && threadIdx.x < 64)
     __hip_atomic_store(gptr(&sw->tasks[threadIdx.x]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool moe_mode = p.mode == kModeMoe;
-  Tracer tr{p.trace};
+  const bool moe_mode = mode == kModeMoe;
   tr.mark();
-  for (int l = 0; l < p.n_layers; l++) {
-    const dsl_weights w = load_weights(p.w + l);
-    // static indices only: a runtime index into the kernel arguments would copy them to
-    // private memory
-    const dsl_kv kv = l == 0 ? p.kv[0] : l == 1 ? p.kv[1] : l == 2 ? p.kv[2] : p.kv[3];
-    const bool last = l == p.n_layers - 1;
-    const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+  for (int l = 0; l < n_layers; l++) {
+    const bool last = l == n_layers - 1;
     if (!moe_mode) {
-      switch (row_elems(p.h)) {
-        case 1: st_attn_norm_e<1>(p, w, xin, red); break;
-        case 2: st_attn_norm_e<2>(p, w, xin, red); break;
-        case 4: st_attn_norm_e<4>(p, w, xin, red); break;
-        case 8: st_attn_norm_e<8>(p, w, xin, red); break;
-        default: st_attn_norm_e<16>(p, w, xin, red); break;
+      {
+        STAGE(l);
+        const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+        switch (row_elems(p.h)) {
+          case 1: st_attn_norm_e<1>(p, w, xin, red); break;
+          case 2: st_attn_norm_e<2>(p, w, xin, red); break;
+          case 4: st_attn_norm_e<4>(p, w, xin, red); break;
+          case 8: st_attn_norm_e<8>(p, w, xin, red); break;
+          default: st_attn_norm_e<16>(p, w, xin, red); break;
+        }
       }
       grid_barrier(sw, nb);
       tr.mark();
-      linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
-      grid_barrier(sw, nb);
-      tr.mark();
-      st_qkv_post(p, w, kv, red);
-      grid_barrier(sw, nb);
-      tr.mark();
-      linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
-      grid_barrier(sw, nb);
-      tr.mark();
-      switch (p.D) {
-        case 64: st_attention_v<1>(p, cx, kv); break;
-        case 128: st_attention_v<2>(p, cx, kv); break;
-        case 256: st_attention_v<4>(p, cx, kv); break;
-        default: st_attention_v<8>(p, cx, kv); break;
+      {
+        STAGE(l);
+        linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
       }
       grid_barrier(sw, nb);
       tr.mark();
-      switch (p.D) {
-        case 64: st_combine_v<1>(p, cx); break;
-        case 128: st_combine_v<2>(p, cx); break;
-        case 256: st_combine_v<4>(p, cx); break;
-        default: st_combine_v<8>(p, cx); break;
+      {
+        STAGE(l);
+        st_qkv_post(p, w, kv, red);
       }
       grid_barrier(sw, nb);
       tr.mark();
-      linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
-      grid_barrier(sw, nb);
-      tr.mark();
-      switch (row_elems(p.orr)) {
-        case 1: st_t_quant_e<1>(p); break;
-        case 2: st_t_quant_e<2>(p); break;
-        case 4: st_t_quant_e<4>(p); break;
-        case 8: st_t_quant_e<8>(p); break;
-        default: st_t_quant_e<16>(p); break;
+      {
+        STAGE(l);
+        linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
       }
       grid_barrier(sw, nb);
       tr.mark();
-      linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
+      {
+        STAGE(l);
+        switch (p.D) {
+          case 64: st_attention_v<1>(p, cx, kv); break;
+          case 128: st_attention_v<2>(p, cx, kv); break;
+          case 256: st_attention_v<4>(p, cx, kv); break;
+          default: st_attention_v<8>(p, cx, kv); break;
+        }
+      }
       grid_barrier(sw, nb);
       tr.mark();
-      switch (row_elems(p.h)) {
-        case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
-        case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
-        case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
-        case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
-        default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+      {
+        STAGE(l);
+        switch (p.D) {
+          case 64: st_combine_v<1>(p, cx); break;
+          case 128: st_combine_v<2>(p, cx); break;
+          case 256: st_combine_v<4>(p, cx); break;
+          default: st_combine_v<8>(p, cx); break;
+        }
       }
-      if (p.mode == kModeAttn) {
+      grid_barrier(sw, nb);
+      tr.mark();
+      {
+        STAGE(l);
+        linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
+      }
+      grid_barrier(sw, nb);
+      tr.mark();
+      {
+        STAGE(l);
+        switch (row_elems(p.orr)) {
+          case 1: st_t_quant_e<1>(p); break;
+          case 2: st_t_quant_e<2>(p); break;
+          case 4: st_t_quant_e<4>(p); break;
+          case 8: st_t_quant_e<8>(p); break;
+          default: st_t_quant_e<16>(p); break;
+        }
+      }
+      grid_barrier(sw, nb);
+      tr.mark();
+      {
+        STAGE(l);
+        linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
+      }
+      grid_barrier(sw, nb);
+      tr.mark();
+      {
+        STAGE(l);
+        const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+        switch (row_elems(p.h)) {
+          case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
+          case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
+          case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
+          case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
+          default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+        }
+      }
+      if (mode == kModeAttn) {
         tr.mark();
         return;
       }
       grid_barrier(sw, nb);
       tr.mark();
     }
-    const uint16_t *u = moe_mode ? p.x : p.s.u;
-    st_router_shared(p, cx, w, u);
-    grid_barrier(sw, nb);
-      tr.mark();
-    build_routing(p, cx, R, moe_mode);
-    tr.mark();
-    if (blockIdx.x == 0 && p.taps.layer_ids)
-      for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) stg(p.taps.layer_ids + (size_t)l * p.M * p.k + t, R.ids[t]);
-    if (blockIdx.x == 0 && last) {
-      for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) {
-        if (p.taps.topk_ids) stg(p.taps.topk_ids + t, R.ids[t]);
-        if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
-      }
-      if (p.taps.logits)
-        for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
+    {
+      STAGE(l);
+      st_router_shared(p, cx, w, moe_mode ? p.x : p.s.u);
     }
-    st_shared_swiglu(p, moe_mode);
+    grid_barrier(sw, nb);
     tr.mark();
-    st_routed_gate_up(p, cx, w, R, u, &sw->tasks[2 * l]);
+    {
+      STAGE(l);
+      build_routing(p, cx, R, moe_mode);
+      tr.mark();
+      if (blockIdx.x == 0 && p.taps.layer_ids)
+        for (int t = threadIdx.x; t < p.M * p.k; t += kThreads)
+          stg(p.taps.layer_ids + (size_t)l * p.M * p.k + t, R.ids[t]);
+      if (blockIdx.x == 0 && last) {
+        for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) {
+          if (p.taps.topk_ids) stg(p.taps.topk_ids + t, R.ids[t]);
+          if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
+        }
+        if (p.taps.logits)
+          for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
+      }
+    }
+    {
+      STAGE(l);
+      st_shared_swiglu(p, moe_mode);
+    }
+    tr.mark();
+    {
+      STAGE(l);
+      st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u);
+    }
     __syncthreads();
     tr.mark();
     grid_barrier(sw, nb);
-      tr.mark();
-    st_down(p, cx, w, R, &sw->tasks[2 * l + 1]);
+    tr.mark();
+    {
+      STAGE(l);
+      st_down(p, cx, w, R);
+    }
     __syncthreads();
     tr.mark();
     grid_barrier(sw, nb);
-      tr.mark();
-    st_combine_out(p, R, moe_mode, last, last ? p.out : p.s.xin);
+    tr.mark();
+    {
+      STAGE(l);
+      st_combine_out(p, R, moe_mode, last, last ? p.out : p.s.xin);
+    }
     if (!last) {
       grid_barrier(sw, nb);
       tr.mark();
     }
-      tr.mark();
+    tr.mark();
   }
 }
+
+#undef STAGE
 
 }  // namespace dsl
 
