@@ -127,8 +127,44 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gptr(T *p) {
 }
 template <class T>
 __device__ __forceinline__ T ldg(const T *p) { return *gptr(p); }
+// Stores are write-through at device scope (relaxed agent-scope atomic stores, which
+// gfx950 issues with the sc1 policy): a line another XCD reads later never sits dirty
+// in the writer's L2.  Loads are plain.  Together with the rule that every buffer the
+// launch produces is written at most once per launch and read only after the grid
+// barrier that follows the write, no cache can hold a stale copy of produced data, so
+// the grid barrier needs no L2 write-back or invalidate.
+template <class U>
+__device__ __forceinline__ void st_wt(U *p, U v) {
+  __hip_atomic_store(gptr(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 template <class T>
-__device__ __forceinline__ void stg(T *p, T v) { *gptr(p) = v; }
+__device__ __forceinline__ void stg(T *p, T v) {
+  static_assert(sizeof(T) == 1 || sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8 || sizeof(T) == 16,
+                "store size");
+  if constexpr (sizeof(T) == 16) {
+    uint64_t w[2];
+    __builtin_memcpy(w, &v, 16);
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    st_wt(q, w[0]);
+    st_wt(q + 1, w[1]);
+  } else if constexpr (sizeof(T) == 8) {
+    uint64_t w;
+    __builtin_memcpy(&w, &v, 8);
+    st_wt(reinterpret_cast<uint64_t *>(p), w);
+  } else if constexpr (sizeof(T) == 4) {
+    uint32_t w;
+    __builtin_memcpy(&w, &v, 4);
+    st_wt(reinterpret_cast<uint32_t *>(p), w);
+  } else if constexpr (sizeof(T) == 2) {
+    uint16_t w;
+    __builtin_memcpy(&w, &v, 2);
+    st_wt(reinterpret_cast<uint16_t *>(p), w);
+  } else {
+    uint8_t w;
+    __builtin_memcpy(&w, &v, 1);
+    st_wt(reinterpret_cast<uint8_t *>(p), w);
+  }
+}
 __device__ __forceinline__ v4u ld16(const void *p) { return ldg(reinterpret_cast<const v4u *>(p)); }
 __device__ __forceinline__ void st16(void *p, v4u v) { stg(reinterpret_cast<v4u *>(p), v); }
 __device__ __forceinline__ float4 ld_f4(const float *p) {
@@ -157,35 +193,36 @@ struct SyncWords {
 
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 
-// All blocks of the launch meet here.  Writes before the barrier are visible to
-// every block after it (agent-scope release by each arriving block, acquire after).
-// Arrivals are counted in two levels (8 group counters, then one top counter) so no
-// single address takes more than nblocks/8 atomics.  The spin is bounded: a barrier
-// that does not complete records kFaultBarrier in the health word and lets the block
-// go on, so the launch always drains.
+// All blocks of the launch meet here.  Each wave first waits for its own memory
+// operations (its write-through stores are then at the device's coherence point), the
+// block meets, and thread 0 arrives with relaxed atomics.  Arrivals are counted in two
+// levels (8 group counters, then one top counter) so no single address takes more than
+// nblocks/8 atomics; the last arrival bumps the generation word the others poll.  No
+// cache maintenance: see stg.  The spin is bounded: a barrier that does not complete
+// records kFaultBarrier in the health word and lets the block go on, so the launch
+// always drains.
 __device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks) {
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned grp = blockIdx.x & 7u;
     const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
     const unsigned per = (nblocks - grp + 7u) / 8u;  // blocks in this group
     const unsigned gen = __hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // release: this block's writes become visible before its arrival is counted
-    const unsigned a = __hip_atomic_fetch_add(gptr(&sw->group[grp][0]), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned a = __hip_atomic_fetch_add(gptr(&sw->group[grp][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool released = false;
     if (a == per - 1u) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(gptr(&sw->group[grp][0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned b = __hip_atomic_fetch_add(gptr(&sw->top[0]), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned b = __hip_atomic_fetch_add(gptr(&sw->top[0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (b == ngroups - 1u) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         __hip_atomic_store(gptr(&sw->top[0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(gptr(&sw->generation), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_fetch_add(gptr(&sw->generation), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         released = true;
       }
     }
     if (!released) {
-      // poll without cache maintenance; one acquire once the generation moved
       unsigned spins = 0;
       while (__hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
         __builtin_amdgcn_s_sleep(1);
@@ -195,7 +232,6 @@ __device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks) {
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }

@@ -708,10 +708,24 @@ __device__ __forceinline__ T kload(const __attribute__((address_space(4))) T *sr
   return v;
 }
 
+// Every member of Scratch is a pointer into one allocation
+__device__ __forceinline__ Scratch shift_scratch(Scratch s, long long off) {
+  static_assert(sizeof(Scratch) % 8 == 0, "scratch descriptor");
+  uint64_t *w = reinterpret_cast<uint64_t *>(&s);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Scratch) / 8); i++) w[i] += (uint64_t)off;
+  return s;
+}
+
+// Layer l's view: its weights, its cache, its own scratch (each layer writes its
+// scratch once per launch), its input (x, or the previous layer's output in this
+// layer's scratch) and where its output goes (out, or the next layer's scratch).
 struct StageArgs {
   Params p;
   dsl_weights w;
   dsl_kv kv;
+  const uint16_t *xin;
+  uint16_t *xout;
 };
 
 __device__ __forceinline__ StageArgs stage_args(int l) {
@@ -720,6 +734,10 @@ __device__ __forceinline__ StageArgs stage_args(int l) {
   a.p = kload(kp);
   a.w = kload((KWeights *)kp->w + l);
   a.kv = kload(&kp->kv[l]);
+  const Scratch s0 = a.p.s;
+  a.p.s = shift_scratch(s0, l * a.p.s_stride);
+  a.xin = l == 0 ? a.p.x : a.p.s.xin;
+  a.xout = l == a.p.n_layers - 1 ? a.p.out : shift_scratch(s0, (l + 1) * a.p.s_stride).xin;
   return a;
 }
 
@@ -729,7 +747,7 @@ struct Tracer {
   unsigned long long *buf = nullptr;
   int n = 0;
   __device__ __forceinline__ void mark() {
-    if (buf && blockIdx.x == 0 && threadIdx.x == 0) buf[n] = wall_clock64();
+    if (buf && blockIdx.x == 0 && threadIdx.x == 0) stg(buf + n, (unsigned long long)wall_clock64());
     n++;
   }
 };
@@ -762,7 +780,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     if (!moe_mode) {
       {
         STAGE(l);
-        const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+        const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
           case 1: st_attn_norm_e<1>(p, w, xin, red); break;
           case 2: st_attn_norm_e<2>(p, w, xin, red); break;
@@ -839,7 +857,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       tr.mark();
       {
         STAGE(l);
-        const uint16_t *xin = l == 0 ? p.x : p.s.xin;
+        const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
           case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
           case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
@@ -900,7 +918,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     tr.mark();
     {
       STAGE(l);
-      st_combine_out(p, R, moe_mode, last, last ? p.out : p.s.xin);
+      st_combine_out(p, R, moe_mode, last, A_.xout);
     }
     if (!last) {
       grid_barrier(sw, nb);
@@ -921,6 +939,7 @@ using namespace dsl;
 struct WidthScratch {
   void *buf = nullptr;
   size_t bytes = 0;
+  long long stride = 0;  // bytes between layers' scratch
   Scratch s{};
 };
 
@@ -1024,11 +1043,12 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   return (off + 255) & ~(size_t)255;
 }
 
-static int get_width(dsl_layer *L, int M, Scratch *out) {
+static int get_width(dsl_layer *L, int M, Scratch *out, long long *stride) {
   WidthScratch &w = L->wid[M];
   if (!w.buf) {
     Scratch tmp;
-    const size_t bytes = layout(L, M, &tmp, nullptr);
+    const size_t per_layer = layout(L, M, &tmp, nullptr);
+    const size_t bytes = per_layer * L->d.n_layers;
     HIPCHK(hipSetDevice(L->dev));
     if (hipMalloc(&w.buf, bytes) != hipSuccess) {
       w.buf = nullptr;
@@ -1036,9 +1056,11 @@ static int get_width(dsl_layer *L, int M, Scratch *out) {
     }
     HIPCHK(hipMemset(w.buf, 0, bytes));
     w.bytes = bytes;
+    w.stride = (long long)per_layer;
     layout(L, M, &w.s, (char *)w.buf);
   }
   *out = w.s;
+  *stride = w.stride;
   return 0;
 }
 
@@ -1110,7 +1132,8 @@ int dsl_layer_reserve(dsl_layer *L, int32_t M) {
   if (!L) return fail(DSL_EINVAL, "layer is NULL");
   if (M < 1 || M > L->d.max_rows) return fail(DSL_EUNSUPPORTED, "width %d outside 1..%d", M, L->d.max_rows);
   Scratch s;
-  return get_width(L, M, &s);
+  long long stride;
+  return get_width(L, M, &s, &stride);
 }
 
 static int check_kv(const dsl_layer *L, const dsl_kv *kv, int n) {
@@ -1128,6 +1151,14 @@ static int check_kv(const dsl_layer *L, const dsl_kv *kv, int n) {
       return fail(DSL_EINVAL, "kv[%d]: n_blocks, max_blocks and n_req must be positive", l);
     if (d.swa_width > 0 && !c.key_table) return fail(DSL_EINVAL, "kv[%d]: index-table mode needs key_table", l);
   }
+  // a launch writes each record once and reads it only after the barrier that follows:
+  // two layers sharing cache memory would break that
+  for (int a = 0; a < n; a++)
+    for (int b = a + 1; b < n; b++) {
+      const uintptr_t a0 = (uintptr_t)kv[a].base, a1 = a0 + (uintptr_t)(kv[a].n_blocks * kv[a].block_stride);
+      const uintptr_t b0 = (uintptr_t)kv[b].base, b1 = b0 + (uintptr_t)(kv[b].n_blocks * kv[b].block_stride);
+      if (a0 < b1 && b0 < a1) return fail(DSL_EINVAL, "kv[%d] and kv[%d] overlap: every layer needs a cache of its own", a, b);
+    }
   return 0;
 }
 
@@ -1144,7 +1175,7 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
     if ((rc = check_kv(L, kv, nl))) return rc;
   }
   Params p{};
-  if ((rc = get_width(L, M, &p.s))) return rc;
+  if ((rc = get_width(L, M, &p.s, &p.s_stride))) return rc;
   const dsl_dims &d = L->d;
   p.h = d.hidden; p.H = d.n_heads; p.D = d.head_dim; p.qr = d.q_rank; p.orr = d.o_rank;
   p.W = d.window; p.swa = d.swa_width; p.E = d.n_experts; p.k = d.top_k; p.I = d.inter;

@@ -67,7 +67,8 @@ struct Params {
   const uint16_t *x;
   uint16_t *out;
   dsl_taps taps;
-  Scratch s;
+  Scratch s;             // layer 0's scratch; layer l's is s shifted by l * s_stride bytes
+  long long s_stride;
   SyncWords *sync;
   unsigned long long *trace;  // per-stage timestamps of block 0, or null
 };
