@@ -27,9 +27,9 @@ namespace dsl {
 // RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values)
 template <int E>
 __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, float *red) {
-  const int n = p.h, k = threadIdx.x * E;
+  const int n = p.h, k = tid() * E;
   const bool act = k < n;
-  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+  for (int m = bid(); m < p.M; m += gridDim.x) {
     float v[E];
     if (act)
       load_bf16<E>(xin + (size_t)m * n + k, v);
@@ -70,7 +70,7 @@ __device__ __forceinline__ int64_t slot_of(const Params &p, const dsl_kv &kv, in
 // q latent: sum the split-K partials, RMSNorm, MXFP8.
 template <int E>
 __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red) {
-  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.qr, k = threadIdx.x * E;
+  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.qr, k = tid() * E;
   const bool act = k < n;
   float v[E];
   if (act)
@@ -93,7 +93,7 @@ __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w,
 // zero bytes) at the row's slot.
 template <int E>
 __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w, const dsl_kv &kv, int m, float *red) {
-  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = threadIdx.x * E;
+  const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = tid() * E;
   const bool act = k < n;
   float v[E];
   if (act)
@@ -117,9 +117,9 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
   if (pos < 0) return;  // pad row: no KV write
   const float sc = am / 448.0f;
   uint8_t *rec = nullptr;
-  if (threadIdx.x == 0) rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
+  if (tid() == 0) rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
   __syncthreads();
-  if (threadIdx.x == 0) red[8] = __uint_as_float((uint32_t)(rec ? 1u : 0u));
+  if (tid() == 0) red[8] = __uint_as_float((uint32_t)(rec ? 1u : 0u));
   __syncthreads();
   if (red[8] == 0.f) return;
   rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
@@ -127,12 +127,12 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 #pragma unroll
     for (int e = 0; e < E; e++) stg(rec + k + e, sc > 0.f ? (uint8_t)f32_to_e4m3(v[e] / sc) : (uint8_t)0);
   }
-  if (threadIdx.x == 0) st16(rec + p.D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
+  if (tid() == 0) st16(rec + p.D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
 }
 
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red) {
   const int eq = row_elems(p.qr), ekv = row_elems(p.D);
-  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+  for (int m = bid(); m < p.M; m += gridDim.x) {
     switch (eq) {
       case 1: qpost_row<1>(p, w, m, red); break;
       case 2: qpost_row<2>(p, w, m, red); break;
@@ -335,9 +335,9 @@ __device__ __forceinline__ void st_combine_v(const Params &p, const Ctx &cx) {
 // wo_a output: sum the split-K partials, then MXFP8
 template <int E>
 __device__ __forceinline__ void st_t_quant_e(const Params &p) {
-  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa, k = threadIdx.x * E;
+  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa, k = tid() * E;
   const bool act = k < N;
-  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+  for (int m = bid(); m < p.M; m += gridDim.x) {
     float v[E];
     if (act)
       load_sum_f32<E>(p.s.p_t + (size_t)m * N + k, (size_t)p.M * N, nks, v);
@@ -353,9 +353,9 @@ __device__ __forceinline__ void st_t_quant_e(const Params &p) {
 // hres = bf16(x + a), u = bf16(RMSNorm_ffn(hres)).  Pad rows give zeros.
 template <int E>
 __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, bool last, float *red) {
-  const int h = p.h, nks = p.orr / p.pl.kc_ob, k = threadIdx.x * E;
+  const int h = p.h, nks = p.orr / p.pl.kc_ob, k = tid() * E;
   const bool act = k < h;
-  for (int m = blockIdx.x; m < p.M; m += gridDim.x) {
+  for (int m = bid(); m < p.M; m += gridDim.x) {
     const bool live = ldg(p.pos + m) >= 0;
     float a[E], hr[E];
     if (act) {
@@ -442,7 +442,7 @@ constexpr int kRowsPerWave = (DSL_MAX_ROWS + kWavesPerBlock - 1) / kWavesPerBloc
 
 __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
   const int k = p.k, E = p.E, M = p.M, lane = cx.lane;
-  for (int e = threadIdx.x; e < 128; e += kThreads) R.cnt[e] = 0;
+  for (int e = tid(); e < 128; e += kThreads) R.cnt[e] = 0;
   // every logit load of this wave's rows in flight at once
   float l0[kRowsPerWave], l1[kRowsPerWave];
   bool live[kRowsPerWave];
@@ -528,7 +528,7 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
   // rank of pair t among the earlier pairs of its expert (ids of one row are distinct, so
   // earlier pairs are earlier rows)
   const int P = M * k;
-  for (int t = threadIdx.x; t < P; t += kThreads) {
+  for (int t = tid(); t < P; t += kThreads) {
     const int id = R.ids[t];
     if (id < 0) continue;
     const int m = t / k;
@@ -546,7 +546,7 @@ __device__ __forceinline__ void st_shared_swiglu(const Params &p, bool all_live)
   const int Is = p.Is, nks = p.h / p.pl.kc_sh13;
   const size_t pstride = (size_t)p.M * 2 * Is;
   const int total = p.M * Is;
-  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+  for (int idx = bid() * kThreads + tid(); idx < total; idx += gridDim.x * kThreads) {
     const int m = idx / Is, n = idx - m * Is;
     float z = 0.f;
     if (all_live || ldg(p.pos + m) >= 0) {
@@ -619,16 +619,252 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
   }
 }
 
+// ------------------------------------------------------------ routed experts on the VALU
+//
+// An expert that few rows selected is a weight-streaming GEMV: the MXFP4 rows are read
+// once and the handful of activation rows are held in registers for the whole task.
+// Lane l takes 32-element block l + 64 q of every weight row (q < Q, K = 2048 Q), so
+// each load instruction of the wave reads 1 KB of one row contiguously.  A 16-byte
+// load holds 32 e2m1 codes; each byte is decoded with its block's E8M0 scale into two
+// exact bf16 and multiplied into f32 with a bf16 dot product.  Lane partials of 16
+// (row, activation row) outputs are then summed across the wave by a transposing
+// butterfly, after which lane L holds the total of output L >> 2.
+
+// Sum over the wave of V per-lane values, transposed: returns, in lane L, the total of
+// value L >> (6 - log2 V).  Lane bit 5 is resolved by a permlane32 swap, bit 4 by a
+// permlane16 swap (for a pair (A, B) both halves then hold A and B summed over the
+// bit), the lower bits by shuffles.
+template <int V>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V is a power of two");
+  float c[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) c[i] = v[i];
+  int n = V;
+#pragma unroll
+  for (int i = 0; i < V / 2; i++) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 2]), false, false);
+    c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (V >= 2) n = V / 2;
+  if (V >= 4) {
+#pragma unroll
+    for (int i = 0; i < V / 4; i++) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 4]), false, false);
+      c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    n = V / 4;
+  }
+#pragma unroll
+  for (int bit = 3; bit >= 0; bit--) {
+    if (n >= 2) {
+      const bool hi = (lane >> bit) & 1;
+#pragma unroll
+      for (int i = 0; i < n / 2; i++) {
+        const float send = hi ? c[i] : c[i + n / 2];
+        const float keep = hi ? c[i + n / 2] : c[i];
+        c[i] = keep + __shfl_xor(send, 1 << bit, kWave);
+      }
+      n /= 2;
+    } else {
+      c[0] += __shfl_xor(c[0], 1 << bit, kWave);
+    }
+  }
+  if (V == 1) {
+    // bits 5 and 4 were not reduced above
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
+    c[0] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
+    c[0] = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  }
+  return c[0];
+}
+
+// acc[v] += dot(weights of one 16-byte load, activations) for one weight row
+template <int CE, int Q>
+__device__ __forceinline__ void valu_row(const v4u &wv, float scale, const uint32_t (&xq)[CE][16], float *acc) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t wp0 = cvt_fp4x2_bf16<0>(wv[i], scale), wp1 = cvt_fp4x2_bf16<1>(wv[i], scale);
+    const uint32_t wp2 = cvt_fp4x2_bf16<2>(wv[i], scale), wp3 = cvt_fp4x2_bf16<3>(wv[i], scale);
+#pragma unroll
+    for (int m = 0; m < CE; m++) {
+      float a = acc[m];
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wp0), __builtin_bit_cast(v2bf, xq[m][4 * i + 0]), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wp1), __builtin_bit_cast(v2bf, xq[m][4 * i + 1]), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wp2), __builtin_bit_cast(v2bf, xq[m][4 * i + 2]), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wp3), __builtin_bit_cast(v2bf, xq[m][4 * i + 3]), a, false);
+      acc[m] = a;
+    }
+  }
+}
+
+// The lane's activation words of CE rows (blocks lane + 64 q, q < Q): 16 words per block
+template <int CE, int Q>
+__device__ __forceinline__ void valu_load_x(const uint16_t *const (&rows)[CE], int lane, uint32_t (&xv)[Q][CE][16]) {
+#pragma unroll
+  for (int q = 0; q < Q; q++)
+#pragma unroll
+    for (int m = 0; m < CE; m++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const v4u t = ld16(rows[m] + 32 * (lane + 64 * q) + 8 * c);
+        xv[q][m][4 * c + 0] = t[0]; xv[q][m][4 * c + 1] = t[1];
+        xv[q][m][4 * c + 2] = t[2]; xv[q][m][4 * c + 3] = t[3];
+      }
+}
+
+// E8M0 scales of 16 consecutive weight rows (16 x 64 Q bytes) into this wave's LDS
+template <int Q>
+__device__ __forceinline__ void valu_stage_scales(const uint8_t *src, uint8_t *dst, int lane) {
+#pragma unroll
+  for (int c = 0; c < Q; c++) {
+    const v4u t = ld16(src + 16 * (lane + 64 * c));
+    *reinterpret_cast<v4u *>(dst + 16 * (lane + 64 * c)) = t;
+  }
+}
+
+constexpr int kValuDepth = 8;  // weight rows in flight per wave
+
+// Gate/up of one expert for its CE <= 2 rows over a tile of 16 gate and 16 up rows,
+// SwiGLU in the epilogue.  Rows are taken in groups of G = 16 / CE (half gate, half up)
+// so one butterfly sums a group's 16 outputs; gate totals land in lanes 0-31, the
+// matching up totals 32 lanes higher.
+template <int CE, int Q>
+__device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_weights &w, const Routing &R,
+                                                    const uint16_t *u, int e, int p0, int ce, int tile, int lane,
+                                                    uint8_t *sl) {
+  constexpr int NB = 64 * Q;   // 32-blocks per weight row
+  constexpr int G = 16 / CE;   // rows per group
+  constexpr int H = G / 2;     // gate (and up) rows per group
+  constexpr int NR = 32;       // rows per task
+  constexpr int DEPTH = kValuDepth / Q;
+  const int h = p.h, I = p.I;
+  const size_t row_bytes = (size_t)h >> 1;
+  const uint8_t *W = w.ex_w13 + (size_t)e * (2 * I) * row_bytes;
+  const uint8_t *S = w.ex_w13_s + (size_t)e * (2 * I) * NB;
+  const uint16_t *rows[CE];
+#pragma unroll
+  for (int m = 0; m < CE; m++) rows[m] = u + (size_t)R.pair_row[p0 + (m < ce ? m : 0)] * h;
+  uint32_t xv[Q][CE][16];
+  valu_load_x<CE, Q>(rows, lane, xv);
+  valu_stage_scales<Q>(S + (size_t)(tile * 16) * NB, sl, lane);
+  valu_stage_scales<Q>(S + (size_t)(I + tile * 16) * NB, sl + 16 * NB, lane);
+  // weight row r of the task in processing order: group r / G, gate rows then up rows
+  auto row_of = [&](int r) -> int {
+    const int gi = r / G, rr = r % G;
+    return (rr >= H ? I : 0) + tile * 16 + gi * H + rr % H;
+  };
+  v4u ring[DEPTH][Q];
+#pragma unroll
+  for (int r = 0; r < DEPTH; r++)
+#pragma unroll
+    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)row_of(r) * row_bytes + 16 * (lane + 64 * q));
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < NR; r++) {
+    const int gi = r / G, rr = r % G, half = rr >= H ? 1 : 0, n = gi * H + rr % H;
+    if (rr == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[v] = 0.f;
+    }
+    v4u cur[Q];
+#pragma unroll
+    for (int q = 0; q < Q; q++) cur[q] = ring[r % DEPTH][q];
+    if (r + DEPTH < NR) {
+#pragma unroll
+      for (int q = 0; q < Q; q++)
+        ring[r % DEPTH][q] = ld16(W + (size_t)row_of(r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
+    }
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const float sc = e8m0_to_f32(sl[half * 16 * NB + n * NB + lane + 64 * q]);
+      valu_row<CE, Q>(cur[q], sc, xv[q], acc + (half * H + rr % H) * CE);
+    }
+    if (rr == G - 1) {
+      const float tot = wave_transpose_sum<16>(acc, lane);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+      const float upv = __uint_as_float(sw[1]);
+      const int j = lane >> 2;  // value (half, row, activation row) = (j >> 3, (j & 7) / CE, (j & 7) % CE)
+      const int rl = (j & 7) / CE, m = (j & 7) % CE;
+      if (lane < 32 && (lane & 3) == 0 && m < ce) {
+        stg(p.s.zr + (size_t)(p0 + m) * I + tile * 16 + gi * H + rl, (uint16_t)f32_to_bf16(swiglu_clamp(tot, upv, p.lim)));
+      }
+    }
+  }
+}
+
+// Down projection of one expert for its CE pairs over a tile of 16 output rows
+template <int CE, int Q>
+__device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile,
+                                                 int lane, uint8_t *sl) {
+  constexpr int NB = 64 * Q;
+  constexpr int G = 16 / CE;
+  constexpr int NR = 16;
+  const int h = p.h, I = p.I;
+  const size_t row_bytes = (size_t)I >> 1;
+  const uint8_t *W = w.ex_wd + (size_t)e * h * row_bytes;
+  const uint8_t *S = w.ex_wd_s + (size_t)e * h * NB;
+  const uint16_t *rows[CE];
+#pragma unroll
+  for (int m = 0; m < CE; m++) rows[m] = p.s.zr + (size_t)(p0 + (m < ce ? m : 0)) * I;
+  uint32_t xv[Q][CE][16];
+  valu_load_x<CE, Q>(rows, lane, xv);
+  valu_stage_scales<Q>(S + (size_t)(tile * 16) * NB, sl, lane);
+  constexpr int DEPTH = kValuDepth / Q;
+  v4u ring[DEPTH][Q];
+#pragma unroll
+  for (int r = 0; r < DEPTH; r++)
+#pragma unroll
+    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)(tile * 16 + r) * row_bytes + 16 * (lane + 64 * q));
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < NR; r++) {
+    const int gi = r / G, rr = r % G;
+    if (rr == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[v] = 0.f;
+    }
+    v4u cur[Q];
+#pragma unroll
+    for (int q = 0; q < Q; q++) cur[q] = ring[r % DEPTH][q];
+    if (r + DEPTH < NR) {
+#pragma unroll
+      for (int q = 0; q < Q; q++)
+        ring[r % DEPTH][q] = ld16(W + (size_t)(tile * 16 + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
+    }
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const float sc = e8m0_to_f32(sl[r * NB + lane + 64 * q]);
+      valu_row<CE, Q>(cur[q], sc, xv[q], acc + rr * CE);
+    }
+    if (rr == G - 1) {
+      const float tot = wave_transpose_sum<16>(acc, lane);
+      const int j = lane >> 2;  // value (row, pair) = (j / CE, j % CE)
+      if ((lane & 3) == 0 && j % CE < ce) stg(p.s.y + (size_t)(p0 + j % CE) * h + tile * 16 + gi * G + j / CE, tot);
+    }
+  }
+}
+
 // Routed gate/up tasks (selected expert, 16-row tile of gate and of up) from the queue
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
-                                  const uint16_t *u) {
+                                  const uint16_t *u, uint8_t *sl) {
   const int tiles_n = p.I >> 4;
   const int T = R.nd * tiles_n;
+  const int qv = p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
-    if (ncg == 1)
+    if (qv && ce <= 2) {
+      if (qv == 1) {
+        if (ce == 1) routed_gate_up_valu<1, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+        else routed_gate_up_valu<2, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+      } else {
+        if (ce == 1) routed_gate_up_valu<1, 2>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+        else routed_gate_up_valu<2, 2>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+      }
+    } else if (ncg == 1)
       routed_gate_up_task<1>(p, w, R, u, e, p0, ce, tile, cx.lane);
     else if (ncg == 2)
       routed_gate_up_task<2>(p, w, R, u, e, p0, ce, tile, cx.lane);
@@ -638,17 +874,26 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
 }
 
 // Shared down partials (static split), then routed down tasks from the queue
-__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R) {
+__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
+                                        uint8_t *sl) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
   for (int t = cx.gw; t < TS; t += cx.nw)
     linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
   const int tiles_n = p.h >> 4;
   const int T = R.nd * tiles_n;
+  const int qv = p.I == 2048 ? 1 : p.I == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
     const int ncg = (ce + 15) >> 4;
-    if (ncg == 1)
+    if (qv == 1 && ce <= 4) {
+      if (ce == 1) routed_down_valu<1, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else if (ce == 2) routed_down_valu<2, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else routed_down_valu<4, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
+    } else if (qv == 2 && ce <= 2) {
+      if (ce == 1) routed_down_valu<1, 2>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else routed_down_valu<2, 2>(p, w, e, p0, ce, tile, cx.lane, sl);
+    } else if (ncg == 1)
       routed_down_task<1>(p, w, e, p0, ce, tile, cx.lane);
     else if (ncg == 2)
       routed_down_task<2>(p, w, e, p0, ce, tile, cx.lane);
@@ -663,7 +908,7 @@ __device__ __forceinline__ void st_combine_out(const Params &p, const Routing &R
   const int h = p.h, k = p.k, nks = p.Is / p.pl.kc_shd;
   const size_t pstride = (size_t)p.M * h;
   const int total = p.M * h;
-  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
+  for (int idx = bid() * kThreads + tid(); idx < total; idx += gridDim.x * kThreads) {
     const int m = idx / h, n = idx - m * h;
     const bool live = moe_mode || ldg(p.pos + m) >= 0;
     float mo = 0.f;
@@ -747,19 +992,19 @@ struct Tracer {
   unsigned long long *buf = nullptr;
   int n = 0;
   __device__ __forceinline__ void mark() {
-    if (buf && blockIdx.x == 0 && threadIdx.x == 0) stg(buf + n, (unsigned long long)wall_clock64());
+    if (buf && bid() == 0 && tid() == 0) stg(buf + n, (unsigned long long)wall_clock64());
     n++;
   }
 };
 
 #define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
-  const dsl_kv &kv = A_.kv; (void)p; (void)w; (void)kv
+  const dsl_kv &kv = A_.kv; const Ctx cx = make_ctx(); (void)p; (void)w; (void)kv; (void)cx
 
 __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   (void)p_arg;
   __shared__ Routing R;
   __shared__ float red[16];
-  const Ctx cx = make_ctx();
+  __shared__ __attribute__((aligned(16))) uint8_t wave_lds[kWavesPerBlock][4096];  // per-wave scale staging
   const unsigned nb = gridDim.x;
   int mode, n_layers;
   SyncWords *sw;
@@ -771,8 +1016,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     sw = kp->sync;
     tr.buf = kp->trace;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 64)
-    __hip_atomic_store(gptr(&sw->tasks[threadIdx.x]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (bid() == 0 && tid() < 64)
+    __hip_atomic_store(gptr(&sw->tasks[tid()]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool moe_mode = mode == kModeMoe;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
@@ -883,16 +1128,16 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       STAGE(l);
       build_routing(p, cx, R, moe_mode);
       tr.mark();
-      if (blockIdx.x == 0 && p.taps.layer_ids)
-        for (int t = threadIdx.x; t < p.M * p.k; t += kThreads)
+      if (bid() == 0 && p.taps.layer_ids)
+        for (int t = tid(); t < p.M * p.k; t += kThreads)
           stg(p.taps.layer_ids + (size_t)l * p.M * p.k + t, R.ids[t]);
-      if (blockIdx.x == 0 && last) {
-        for (int t = threadIdx.x; t < p.M * p.k; t += kThreads) {
+      if (bid() == 0 && last) {
+        for (int t = tid(); t < p.M * p.k; t += kThreads) {
           if (p.taps.topk_ids) stg(p.taps.topk_ids + t, R.ids[t]);
           if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
         }
         if (p.taps.logits)
-          for (int t = threadIdx.x; t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
+          for (int t = tid(); t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
       }
     }
     {
@@ -902,7 +1147,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     tr.mark();
     {
       STAGE(l);
-      st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u);
+      st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
     }
     __syncthreads();
     tr.mark();
@@ -910,7 +1155,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     tr.mark();
     {
       STAGE(l);
-      st_down(p, cx, w, R);
+      st_down(p, cx, w, R, wave_lds[cx.wave]);
     }
     __syncthreads();
     tr.mark();

@@ -87,11 +87,27 @@ struct Ctx {
   int lane, wave, gw, nw;  // lane, wave in block, global wave id, waves in grid
 };
 
+// The thread index through an empty asm: values derived from it are then recomputed in
+// each stage instead of being hoisted out of the layer loop and kept live (spilled)
+// across the whole launch.
+__device__ __forceinline__ int tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ int bid() {
+  int b = blockIdx.x;
+  asm volatile("" : "+s"(b));
+  return b;
+}
+
 __device__ __forceinline__ Ctx make_ctx() {
   Ctx c;
-  c.lane = threadIdx.x & 63;
-  c.wave = threadIdx.x >> 6;
-  c.gw = blockIdx.x * kWavesPerBlock + c.wave;
+  const int t = tid();
+  c.lane = t & 63;
+  c.wave = t >> 6;
+  c.gw = bid() * kWavesPerBlock + c.wave;
   c.nw = gridDim.x * kWavesPerBlock;
   return c;
 }
@@ -375,14 +391,14 @@ __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, cons
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((tid() & 63) == 0) red[tid() >> 6] = v;
   __syncthreads();
   return ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
 }
 __device__ __forceinline__ float block_max(float v, float *red) {
   v = wave_max(v);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((tid() & 63) == 0) red[tid() >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
 }
