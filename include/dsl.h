@@ -173,13 +173,16 @@ int dsl_moe_step(dsl_layer *layer, const void *u_bf16, int32_t M, void *moe_out_
  * is then cleared and the handle's sync state reset). */
 int dsl_layer_health(dsl_layer *layer);
 
-/* Tracing for profiling: with on != 0, block 0 of every later launch stamps the
- * device wall clock at the launch's start, after each grid barrier (one stamp per
- * stage boundary) and at its end.  dsl_layer_read_trace copies the stamps of the
- * most recent traced launch (call after synchronizing) as nanoseconds since its
- * start into ns[0..n) and returns how many it wrote. */
+/* Tracing for profiling: with on != 0, thread 0 of every block of every later
+ * launch stamps the device wall clock at the launch's start, on arriving at and on
+ * leaving each grid barrier, at a few points inside the MoE stage and at the end.
+ * dsl_layer_read_trace copies the stamps of the most recent traced launch (call
+ * after synchronizing) into ns[mark * grid_blocks + block] as nanoseconds since
+ * block 0's first stamp (-1 where a block wrote none), for up to n_marks marks
+ * (ns holds n_marks * grid_blocks doubles, see dsl_layer_grid), and returns the
+ * number of marks written. */
 int dsl_layer_set_trace(dsl_layer *layer, int32_t on);
-int dsl_layer_read_trace(dsl_layer *layer, double *ns, int32_t n);
+int dsl_layer_read_trace(dsl_layer *layer, double *ns, int32_t n_marks);
 
 /* Grid the persistent launch uses (blocks, threads per block); for reports. */
 int dsl_layer_grid(const dsl_layer *layer, int32_t *blocks, int32_t *threads);

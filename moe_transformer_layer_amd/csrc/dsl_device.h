@@ -110,6 +110,98 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Sum over the wave of V per-lane values, transposed: returns, in lane L, the total of
+// value L >> (6 - log2 V).  Lane bit 5 is resolved by a permlane32 swap, bit 4 by a
+// permlane16 swap (for a pair (A, B) both halves then hold A and B summed over the
+// bit), the lower bits by shuffles.
+template <int V>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V is a power of two");
+  float c[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) c[i] = v[i];
+  int n = V;
+#pragma unroll
+  for (int i = 0; i < V / 2; i++) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 2]), false, false);
+    c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (V >= 2) n = V / 2;
+  if (V >= 4) {
+#pragma unroll
+    for (int i = 0; i < V / 4; i++) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 4]), false, false);
+      c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    n = V / 4;
+  }
+#pragma unroll
+  for (int bit = 3; bit >= 0; bit--) {
+    if (n >= 2) {
+      const bool hi = (lane >> bit) & 1;
+#pragma unroll
+      for (int i = 0; i < n / 2; i++) {
+        const float send = hi ? c[i] : c[i + n / 2];
+        const float keep = hi ? c[i + n / 2] : c[i];
+        c[i] = keep + __shfl_xor(send, 1 << bit, kWave);
+      }
+      n /= 2;
+    } else {
+      c[0] += __shfl_xor(c[0], 1 << bit, kWave);
+    }
+  }
+  if (V == 1) {
+    // bits 5 and 4 were not reduced above
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
+    c[0] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
+    c[0] = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  }
+  return c[0];
+}
+
+// Arg-max keys: an unsigned 64-bit key whose order is (float value, then lower index):
+// high word = the float's bits made order-preserving as an unsigned integer, low word
+// = 127 - index.  Exact for every non-NaN value.
+__device__ __forceinline__ uint64_t amax_key(float v, int i) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(127 - i);
+}
+__device__ __forceinline__ float amax_key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int amax_key_index(uint64_t k) { return 127 - (int)(uint32_t)k; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t amax_dpp(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+// The key of the lane 16 (or 32) positions away across the half boundary
+__device__ __forceinline__ uint64_t amax_half(uint64_t k, bool lower, bool is32) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  const auto rl = is32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                       : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto rh = is32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                       : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const uint64_t o = ((uint64_t)(lower ? rh[1] : rh[0]) << 32) | (lower ? rl[1] : rl[0]);
+  return o > k ? o : k;
+}
+// Wave-wide maximum key, in every lane: quad and row steps by DPP, the 16- and 32-lane
+// halves by the permlane swaps.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k, int lane) {
+  k = amax_dpp<0xB1>(k);   // quad_perm 1,0,3,2
+  k = amax_dpp<0x4E>(k);   // quad_perm 2,3,0,1
+  k = amax_dpp<0x124>(k);  // row_ror 4
+  k = amax_dpp<0x128>(k);  // row_ror 8
+  k = amax_half(k, (lane & 16) == 0, false);
+  return amax_half(k, lane < 32, true);
+}
+
 // ------------------------------------------------------------------ loads / stores
 
 // Every buffer the kernel touches is device (global) memory.  Pointers reach the
@@ -188,7 +280,6 @@ struct SyncWords {
   unsigned pad1[63];
   unsigned health;        // 0, or a DSL device fault code
   unsigned pad2[63];
-  unsigned tasks[64];     // task-queue counters (zeroed at each launch before use)
 };
 
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "dsl_stages.h"
 
@@ -92,7 +93,8 @@ __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w,
 // kv latent: RMSNorm, then the fp8 record (codes e4m3(v / s), s = amax / 448, then 12
 // zero bytes) at the row's slot.
 template <int E>
-__device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w, const dsl_kv &kv, int m, float *red) {
+__device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w, const dsl_kv &kv, int m, float *red,
+                                           uint8_t *tmp) {
   const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = tid() * E;
   const bool act = k < n;
   float v[E];
@@ -123,14 +125,20 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
   __syncthreads();
   if (red[8] == 0.f) return;
   rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
+  // codes gathered in LDS, then written as 16-byte stores
   if (act) {
 #pragma unroll
-    for (int e = 0; e < E; e++) stg(rec + k + e, sc > 0.f ? (uint8_t)f32_to_e4m3(v[e] / sc) : (uint8_t)0);
+    for (int e = 0; e < E; e++) tmp[k + e] = sc > 0.f ? (uint8_t)f32_to_e4m3(v[e] / sc) : (uint8_t)0;
   }
-  if (tid() == 0) st16(rec + p.D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
+  __syncthreads();
+  const int t = tid();
+  if (t < n / 16) st16(rec + 16 * t, *reinterpret_cast<const v4u *>(tmp + 16 * t));
+  if (t == n / 16) st16(rec + p.D, v4u{__float_as_uint(sc), 0u, 0u, 0u});
 }
 
-__device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red) {
+// tmp: LDS of at least head_dim bytes for the record's codes
+__device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
+                                            uint8_t *tmp) {
   const int eq = row_elems(p.qr), ekv = row_elems(p.D);
   for (int m = bid(); m < p.M; m += gridDim.x) {
     switch (eq) {
@@ -141,8 +149,8 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
       default: qpost_row<16>(p, w, m, red); break;
     }
     switch (ekv) {
-      case 1: kvpost_row<1>(p, w, kv, m, red); break;
-      default: kvpost_row<2>(p, w, kv, m, red); break;
+      case 1: kvpost_row<1>(p, w, kv, m, red, tmp); break;
+      default: kvpost_row<2>(p, w, kv, m, red, tmp); break;
     }
   }
 }
@@ -208,12 +216,7 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   const size_t qstride = (size_t)p.M * H * D;
   const float *qp = p.s.p_q + (size_t)m * H * D + (size_t)hh * D + lane * V;
   float q[V];
-#pragma unroll
-  for (int v = 0; v < V; v++) q[v] = ldg(qp + v);
-  for (int ks = 1; ks < nks; ks++) {
-#pragma unroll
-    for (int v = 0; v < V; v++) q[v] += ldg(qp + ks * qstride + v);
-  }
+  load_sum_f32<V>(qp, qstride, nks, q);
   const uint64_t recbits = reinterpret_cast<uint64_t>(myrec);
   constexpr int HALF = kSplitKeys / 2;
   // scores, 16 keys at a time: every lane loads its V dims of the 16 keys at once
@@ -394,57 +397,92 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
 
 // ============================================================== MoE
 
-constexpr int kRouterRows = 4;
-
-// f32 router logits of one expert for up to 4 rows: lane-strided dot products over the
-// whole hidden dimension (the expert's weight row is loaded once), then wave sums.
-__device__ __forceinline__ void router_task(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e, int m0,
-                            int lane) {
-  float acc[kRouterRows] = {0.f, 0.f, 0.f, 0.f};
-  const float *wrow = Wr + (size_t)e * p.h;
-  for (int k = lane * 4; k < p.h; k += 4 * kWave) {
-    const float4 w4 = ld_f4(wrow + k);
+// Router partial logits of one (expert e, K chunk c) task for all rows: lane l takes
+// elements c kc + 512 j + 8 l .. + 8 (j < kc / 512, lanes past the chunk idle), the
+// lane partials of 8 rows at a time are summed across the wave by the transposing
+// butterfly (lane L then holds row L >> 3), written to logits[c][m][e].  Each batch of
+// loads is issued before any arithmetic uses it.
+template <int J>
+__device__ __forceinline__ void router_task_j(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e,
+                                              int c, int lane) {
+  const int h = p.h, kc = p.pl.kc_router;
+  float4 wv[J][2];
+  bool on[J];
 #pragma unroll
-    for (int r = 0; r < kRouterRows; r++) {
-      const int m = m0 + r < p.M ? m0 + r : p.M - 1;
-      const v2u uv = ldg(reinterpret_cast<const v2u *>(u + (size_t)m * p.h + k));
-      acc[r] += w4.x * bf16_to_f32(uv[0] & 0xFFFFu) + w4.y * bf16_to_f32(uv[0] >> 16) +
-                w4.z * bf16_to_f32(uv[1] & 0xFFFFu) + w4.w * bf16_to_f32(uv[1] >> 16);
-    }
+  for (int j = 0; j < J; j++) {
+    const int k = c * kc + 512 * j + 8 * lane;
+    on[j] = 512 * j + 8 * lane < kc;
+    const float *wp = Wr + (size_t)e * h + (on[j] ? k : c * kc);
+    wv[j][0] = ld_f4(wp);
+    wv[j][1] = ld_f4(wp + 4);
   }
+  for (int m0 = 0; m0 < p.M; m0 += 8) {
+    v4u uv[8][J];
 #pragma unroll
-  for (int r = 0; r < kRouterRows; r++) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && m0 + r < p.M) stg(p.s.logits + (size_t)(m0 + r) * p.E + e, s);
+    for (int r = 0; r < 8; r++) {
+      const int m = m0 + r < p.M ? m0 + r : p.M - 1;
+#pragma unroll
+      for (int j = 0; j < J; j++)
+        uv[r][j] = ld16(u + (size_t)m * h + (on[j] ? c * kc + 512 * j + 8 * lane : c * kc));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; j++) {
+        if (!on[j]) continue;
+        const float wf[8] = {wv[j][0].x, wv[j][0].y, wv[j][0].z, wv[j][0].w,
+                             wv[j][1].x, wv[j][1].y, wv[j][1].z, wv[j][1].w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          a = fmaf(wf[2 * q], bf16_to_f32(uv[r][j][q] & 0xFFFFu), a);
+          a = fmaf(wf[2 * q + 1], bf16_to_f32(uv[r][j][q] >> 16), a);
+        }
+      }
+      acc[r] = a;
+    }
+    const float tot = wave_transpose_sum<8>(acc, lane);
+    const int m = m0 + (lane >> 3);
+    if ((lane & 7) == 0 && m < p.M) stg(p.s.logits + ((size_t)c * p.M + m) * p.E + e, tot);
   }
 }
 
-// Router logits ((expert, 4-row group) tasks) and the shared expert's gate/up partials,
-// together: both read only the MoE input.
+// Router partial logits ((expert, K chunk) tasks) and the shared expert's gate/up
+// partials, together: both read only the MoE input.
 __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
-  const int groups = (p.M + kRouterRows - 1) / kRouterRows;
-  const int TR = p.E * groups;
+  const int TR = p.E * (p.h / p.pl.kc_router);
   const int Nsh = 2 * p.Is;
   const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
+  const int J = (p.pl.kc_router + 511) >> 9;
   for (int t = cx.gw; t < TR + TS; t += cx.nw) {
-    if (t < TR)
-      router_task(p, w.w_router, u, t % p.E, (t / p.E) * kRouterRows, cx.lane);
-    else
+    if (t < TR) {
+      const int e = t % p.E, c = t / p.E;
+      if (J == 1)
+        router_task_j<1>(p, w.w_router, u, e, c, cx.lane);
+      else
+        router_task_j<2>(p, w.w_router, u, e, c, cx.lane);
+    } else {
       linear_task<kW8B128>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u, p.M,
                            p.s.p_sh);
+    }
   }
 }
 
-// Top-k of every live row (ties to the lower id, descending order, weights = softmax of
-// the selected logits), then the distinct-expert list and the (row, slot) -> pair map
-// ordered by expert id, then by row.  Every block builds the same routing in its own LDS.
+// Routing of every live row, built by every block in its own LDS.  Wave w takes rows
+// w, w + 8, ...: lane l holds logits l and l + 64 (the router's partials summed in chunk
+// order, so every block gets the same values), top-k by k rounds of wave arg-max (ties
+// to the lower id, emitted in descending order), weights = softmax of the selected
+// logits.  Then per expert the set of rows that chose it, the distinct-expert list in
+// id order and the (row, slot) -> pair map ordered by expert, then by row.
 constexpr int kRowsPerWave = (DSL_MAX_ROWS + kWavesPerBlock - 1) / kWavesPerBlock;
 
-__device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live) {
-  const int k = p.k, E = p.E, M = p.M, lane = cx.lane;
-  for (int e = tid(); e < 128; e += kThreads) R.cnt[e] = 0;
-  // every logit load of this wave's rows in flight at once
-  float l0[kRowsPerWave], l1[kRowsPerWave];
+__device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live,
+                                              float *logits_tap) {
+  const int k = p.k, E = p.E, M = p.M, nc = p.h / p.pl.kc_router, lane = cx.lane, t0 = tid();
+  for (int e = t0; e < 128; e += kThreads) R.rows[e] = 0ull;
+  float a0[kRowsPerWave], a1[kRowsPerWave];
   bool live[kRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; r++) {
@@ -452,10 +490,43 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     const int mc = m < M ? m : M - 1;
     live[r] = m < M && (all_live || ldg(p.pos + mc) >= 0);
     const float *lg = p.s.logits + (size_t)mc * E;
-    l0[r] = lane < E ? ldg(lg + lane) : -INFINITY;
-    l1[r] = lane + 64 < E ? ldg(lg + lane + 64) : -INFINITY;
+    const size_t cs = (size_t)M * E;
+    const float s0 = m < M && lane < E ? sum_strided(lg + lane, cs, nc) : 0.f;
+    const float s1 = m < M && lane + 64 < E ? sum_strided(lg + lane + 64, cs, nc) : 0.f;
+    if (logits_tap && m < M) {
+      if (lane < E) stg(logits_tap + (size_t)m * E + lane, s0);
+      if (lane + 64 < E) stg(logits_tap + (size_t)m * E + lane + 64, s1);
+    }
+    a0[r] = lane < E ? s0 : -INFINITY;
+    a1[r] = lane + 64 < E ? s1 : -INFINITY;
   }
   __syncthreads();
+  int myid[kRowsPerWave];
+  float myval[kRowsPerWave];
+  uint64_t k0[kRowsPerWave], k1[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r++) {
+    myid[r] = -1;
+    myval[r] = -INFINITY;
+    k0[r] = amax_key(a0[r], lane);
+    k1[r] = amax_key(a1[r], lane + 64);
+  }
+  const int nrows = M > cx.wave ? (M - cx.wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
+  const uint64_t taken = 0ull;  // key of a removed entry (below every real key)
+  for (int j = 0; j < k; j++) {
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; r++) {
+      if (r < nrows) {
+        const uint64_t best = wave_max_key(k0[r] > k1[r] ? k0[r] : k1[r], lane);
+        if (lane == j) {
+          myid[r] = amax_key_index(best);
+          myval[r] = amax_key_value(best);
+        }
+        if (k0[r] == best) k0[r] = taken;
+        if (k1[r] == best) k1[r] = taken;
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; r++) {
     const int m = cx.wave + r * kWavesPerBlock;
@@ -467,51 +538,29 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
       }
       continue;
     }
-    float a0 = l0[r], a1 = l1[r];
-    int myid = -1;
-    float myval = -INFINITY;
-    for (int j = 0; j < k; j++) {
-      float bv;
-      int bi;
-      if (a0 >= a1) {
-        bv = a0; bi = lane;
-      } else {
-        bv = a1; bi = lane + 64;
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov; bi = oi;
-        }
-      }
-      if (lane == j) {
-        myid = bi; myval = bv;
-      }
-      if (bi == lane) a0 = -INFINITY;
-      if (bi == lane + 64) a1 = -INFINITY;
-    }
-    const float top = __shfl(myval, 0, kWave);
-    const float ev = lane < k ? expf(myval - top) : 0.f;
+    const float top = __shfl(myval[r], 0, kWave);
+    const float ev = lane < k ? expf(myval[r] - top) : 0.f;
     const float sum = wave_sum(ev);
     if (lane < k) {
-      R.ids[m * k + lane] = myid;
+      R.ids[m * k + lane] = myid[r];
       R.w[m * k + lane] = ev / sum;
-      atomicAdd(&R.cnt[myid], 1);
+      atomicOr(&R.rows[myid[r]], 1ull << m);
     }
   }
   __syncthreads();
-  // starts (exclusive scan of the counts in expert order) and the compacted expert list:
+  // counts, starts (exclusive scan in expert order) and the compacted expert list:
   // wave 0, experts lane and lane + 64
   if (cx.wave == 0) {
-    const int c0 = R.cnt[lane], c1 = R.cnt[lane + 64];
+    const int lane = cx.lane;
+    const int c0 = __popcll(R.rows[lane]), c1 = __popcll(R.rows[lane + 64]);
+    R.cnt[lane] = c0;
+    R.cnt[lane + 64] = c1;
     int s0 = c0, s1 = c1;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-      const int t0 = __shfl_up(s0, o, kWave), t1 = __shfl_up(s1, o, kWave);
+      const int a0 = __shfl_up(s0, o, kWave), a1 = __shfl_up(s1, o, kWave);
       if (lane >= o) {
-        s0 += t0; s1 += t1;
+        s0 += a0; s1 += a1;
       }
     }
     const int tot0 = __shfl(s0, kWave - 1, kWave);
@@ -525,16 +574,12 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     if (lane == 0) R.nd = n0 + __popcll(b1);
   }
   __syncthreads();
-  // rank of pair t among the earlier pairs of its expert (ids of one row are distinct, so
-  // earlier pairs are earlier rows)
-  const int P = M * k;
-  for (int t = tid(); t < P; t += kThreads) {
+  // pair of (row m, slot): the expert's start plus the rows before m that chose it
+  for (int t = t0; t < M * k; t += kThreads) {
     const int id = R.ids[t];
     if (id < 0) continue;
     const int m = t / k;
-    int rank = 0;
-    for (int u = 0; u < m * k; u++) rank += R.ids[u] == id;
-    const int slot = R.start[id] + rank;
+    const int slot = R.start[id] + __popcll(R.rows[id] & ((1ull << m) - 1ull));
     R.pair[t] = slot;
     R.pair_row[slot] = m;
   }
@@ -551,11 +596,7 @@ __device__ __forceinline__ void st_shared_swiglu(const Params &p, bool all_live)
     float z = 0.f;
     if (all_live || ldg(p.pos + m) >= 0) {
       const float *b = p.s.p_sh + (size_t)m * 2 * Is;
-      float g = 0.f, u = 0.f;
-      for (int ks = 0; ks < nks; ks++) {
-        g += ldg(b + ks * pstride + n);
-        u += ldg(b + ks * pstride + Is + n);
-      }
+      const float g = sum_strided(b + n, pstride, nks), u = sum_strided(b + Is + n, pstride, nks);
       z = swiglu_clamp(g, u, p.lim);
     }
     stg(p.s.zsh + idx, (uint16_t)f32_to_bf16(z));
@@ -629,56 +670,6 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
 // exact bf16 and multiplied into f32 with a bf16 dot product.  Lane partials of 16
 // (row, activation row) outputs are then summed across the wave by a transposing
 // butterfly, after which lane L holds the total of output L >> 2.
-
-// Sum over the wave of V per-lane values, transposed: returns, in lane L, the total of
-// value L >> (6 - log2 V).  Lane bit 5 is resolved by a permlane32 swap, bit 4 by a
-// permlane16 swap (for a pair (A, B) both halves then hold A and B summed over the
-// bit), the lower bits by shuffles.
-template <int V>
-__device__ __forceinline__ float wave_transpose_sum(float (&v)[V], int lane) {
-  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V is a power of two");
-  float c[V];
-#pragma unroll
-  for (int i = 0; i < V; i++) c[i] = v[i];
-  int n = V;
-#pragma unroll
-  for (int i = 0; i < V / 2; i++) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 2]), false, false);
-    c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  if (V >= 2) n = V / 2;
-  if (V >= 4) {
-#pragma unroll
-    for (int i = 0; i < V / 4; i++) {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[i]), __float_as_uint(c[i + V / 4]), false, false);
-      c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    n = V / 4;
-  }
-#pragma unroll
-  for (int bit = 3; bit >= 0; bit--) {
-    if (n >= 2) {
-      const bool hi = (lane >> bit) & 1;
-#pragma unroll
-      for (int i = 0; i < n / 2; i++) {
-        const float send = hi ? c[i] : c[i + n / 2];
-        const float keep = hi ? c[i + n / 2] : c[i];
-        c[i] = keep + __shfl_xor(send, 1 << bit, kWave);
-      }
-      n /= 2;
-    } else {
-      c[0] += __shfl_xor(c[0], 1 << bit, kWave);
-    }
-  }
-  if (V == 1) {
-    // bits 5 and 4 were not reduced above
-    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
-    c[0] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(c[0]), __float_as_uint(c[0]), false, false);
-    c[0] = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  }
-  return c[0];
-}
 
 // acc[v] += dot(weights of one 16-byte load, activations) for one weight row
 template <int CE, int Q>
@@ -846,7 +837,7 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   }
 }
 
-// Routed gate/up tasks (selected expert, 16-row tile of gate and of up) from the queue
+// Routed gate/up tasks (selected expert, 16-row tile of gate and of up), task t to wave t mod waves
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                   const uint16_t *u, uint8_t *sl) {
   const int tiles_n = p.I >> 4;
@@ -873,7 +864,7 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
   }
 }
 
-// Shared down partials (static split), then routed down tasks from the queue
+// Shared down partials, then routed down tasks (expert, 16-row tile), task t to wave t mod waves
 __device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                         uint8_t *sl) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
@@ -913,8 +904,13 @@ __device__ __forceinline__ void st_combine_out(const Params &p, const Routing &R
     const bool live = moe_mode || ldg(p.pos + m) >= 0;
     float mo = 0.f;
     if (live) {
-      for (int ks = 0; ks < nks; ks++) mo += ldg(p.s.p_shd + ks * pstride + idx);
-      for (int j = 0; j < k; j++) mo = fmaf(R.w[m * k + j], ldg(p.s.y + (size_t)R.pair[m * k + j] * h + n), mo);
+      float yv[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) yv[j] = j < k ? ldg(p.s.y + (size_t)R.pair[m * k + j] * h + n) : 0.f;
+      mo = sum_strided(p.s.p_shd + idx, pstride, nks);
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (j < k) mo = fmaf(R.w[m * k + j], yv[j], mo);
     }
     if (moe_mode) {
       stg(dst + idx, live ? (uint16_t)f32_to_bf16(mo) : (uint16_t)0);
@@ -986,16 +982,25 @@ __device__ __forceinline__ StageArgs stage_args(int l) {
   return a;
 }
 
-// Block 0 stamps the device wall clock at the start, after every grid barrier and at
-// the end of a launch when tracing is on (one entry per stage boundary).
+// With tracing on, every block stamps the device wall clock at the start of the
+// launch, on arriving at and on leaving every grid barrier, at a few points inside the
+// MoE and at the end: buf[mark][block].
 struct Tracer {
   unsigned long long *buf = nullptr;
   int n = 0;
   __device__ __forceinline__ void mark() {
-    if (buf && bid() == 0 && tid() == 0) stg(buf + n, (unsigned long long)wall_clock64());
+    if (buf && tid() == 0) stg(buf + (size_t)n * gridDim.x + bid(), (unsigned long long)wall_clock64());
     n++;
   }
 };
+
+#define SYNC()                \
+  do {                        \
+    __syncthreads();          \
+    tr.mark();                \
+    grid_barrier(sw, nb);     \
+    tr.mark();                \
+  } while (0)
 
 #define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
   const dsl_kv &kv = A_.kv; const Ctx cx = make_ctx(); (void)p; (void)w; (void)kv; (void)cx
@@ -1016,8 +1021,6 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     sw = kp->sync;
     tr.buf = kp->trace;
   }
-  if (bid() == 0 && tid() < 64)
-    __hip_atomic_store(gptr(&sw->tasks[tid()]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool moe_mode = mode == kModeMoe;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
@@ -1034,26 +1037,22 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_attn_norm_e<16>(p, w, xin, red); break;
         }
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
-        st_qkv_post(p, w, kv, red);
+        st_qkv_post(p, w, kv, red, &wave_lds[0][0]);
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         switch (p.D) {
@@ -1063,8 +1062,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_attention_v<8>(p, cx, kv); break;
         }
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         switch (p.D) {
@@ -1074,14 +1072,12 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_combine_v<8>(p, cx); break;
         }
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         switch (row_elems(p.orr)) {
@@ -1092,14 +1088,12 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_t_quant_e<16>(p); break;
         }
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
       {
         STAGE(l);
         const uint16_t *xin = A_.xin;
@@ -1115,18 +1109,16 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         tr.mark();
         return;
       }
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
     }
     {
       STAGE(l);
       st_router_shared(p, cx, w, moe_mode ? p.x : p.s.u);
     }
-    grid_barrier(sw, nb);
-    tr.mark();
+    SYNC();
     {
       STAGE(l);
-      build_routing(p, cx, R, moe_mode);
+      build_routing(p, cx, R, moe_mode, bid() == 0 && last ? p.taps.logits : nullptr);
       tr.mark();
       if (bid() == 0 && p.taps.layer_ids)
         for (int t = tid(); t < p.M * p.k; t += kThreads)
@@ -1136,8 +1128,6 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           if (p.taps.topk_ids) stg(p.taps.topk_ids + t, R.ids[t]);
           if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
         }
-        if (p.taps.logits)
-          for (int t = tid(); t < p.M * p.E; t += kThreads) stg(p.taps.logits + t, ldg(p.s.logits + t));
       }
     }
     {
@@ -1149,31 +1139,25 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       STAGE(l);
       st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
     }
-    __syncthreads();
-    tr.mark();
-    grid_barrier(sw, nb);
-    tr.mark();
+    SYNC();
     {
       STAGE(l);
       st_down(p, cx, w, R, wave_lds[cx.wave]);
     }
-    __syncthreads();
-    tr.mark();
-    grid_barrier(sw, nb);
-    tr.mark();
+    SYNC();
     {
       STAGE(l);
       st_combine_out(p, R, moe_mode, last, A_.xout);
     }
     if (!last) {
-      grid_barrier(sw, nb);
-      tr.mark();
+      SYNC();
     }
     tr.mark();
   }
 }
 
 #undef STAGE
+#undef SYNC
 
 }  // namespace dsl
 
@@ -1279,7 +1263,7 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   s->xin = (uint16_t *)take(m * h * 2);
   s->hres = (uint16_t *)take(m * h * 2);
   s->u = (uint16_t *)take(m * h * 2);
-  s->logits = (float *)take(m * E * 4);
+  s->logits = (float *)take((h / pl.kc_router) * m * E * 4);
   s->p_sh = (float *)take((h / pl.kc_sh13) * m * 2 * Is * 4);
   s->zsh = (uint16_t *)take(m * Is * 2);
   s->zr = (uint16_t *)take(m * k * I * 2);
@@ -1359,6 +1343,7 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   L->plan.kc_ob = pick_kc(dims->o_rank, 512);
   L->plan.kc_sh13 = pick_kc(dims->hidden, 1024);
   L->plan.kc_shd = pick_kc(dims->shared_inter, 512);
+  L->plan.kc_router = pick_kc(dims->hidden, 1024);
   if (hipMalloc((void **)&L->sync, sizeof(SyncWords)) != hipSuccess ||
       hipMalloc((void **)&L->dw, sizeof(dsl_weights) * dims->n_layers) != hipSuccess) {
     dsl_layer_destroy(L);
@@ -1478,11 +1463,12 @@ int dsl_layer_set_trace(dsl_layer *L, int32_t on) {
   if (!L) return fail(DSL_EINVAL, "layer is NULL");
   HIPCHK(hipSetDevice(L->dev));
   if (on && !L->trace) {
-    if (hipMalloc((void **)&L->trace, kTraceLen * sizeof(unsigned long long)) != hipSuccess) {
+    const size_t bytes = (size_t)kTraceLen * L->grid * sizeof(unsigned long long);
+    if (hipMalloc((void **)&L->trace, bytes) != hipSuccess) {
       L->trace = nullptr;
       return fail(DSL_ENOMEM, "trace buffer allocation failed");
     }
-    HIPCHK(hipMemset(L->trace, 0, kTraceLen * sizeof(unsigned long long)));
+    HIPCHK(hipMemset(L->trace, 0, bytes));
   } else if (!on && L->trace) {
     HIPCHK(hipFree(L->trace));
     L->trace = nullptr;
@@ -1490,19 +1476,25 @@ int dsl_layer_set_trace(dsl_layer *L, int32_t on) {
   return 0;
 }
 
-int dsl_layer_read_trace(dsl_layer *L, double *ns, int32_t n) {
-  if (!L || !ns || n < 0) return fail(DSL_EINVAL, "layer and ns must be set");
+int dsl_layer_read_trace(dsl_layer *L, double *ns, int32_t n_marks) {
+  if (!L || !ns || n_marks < 0) return fail(DSL_EINVAL, "layer and ns must be set");
   if (!L->trace) return fail(DSL_EINVAL, "tracing is off");
-  unsigned long long buf[kTraceLen];
+  const int G = L->grid;
+  std::vector<unsigned long long> buf((size_t)kTraceLen * G);
   HIPCHK(hipSetDevice(L->dev));
-  HIPCHK(hipMemcpy(buf, L->trace, sizeof buf, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(buf.data(), L->trace, buf.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
   int khz = 0;
   HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, L->dev));
   if (khz <= 0) return fail(DSL_EHIP, "device wall clock rate unknown");
   int cnt = 0;
-  while (cnt < kTraceLen && buf[cnt]) cnt++;
-  for (int i = 0; i < cnt && i < n; i++) ns[i] = (double)(buf[i] - buf[0]) * 1e6 / khz;
-  return cnt < n ? cnt : n;
+  while (cnt < kTraceLen && buf[(size_t)cnt * G]) cnt++;
+  const unsigned long long t0 = buf[0];
+  for (int i = 0; i < cnt && i < n_marks; i++)
+    for (int b = 0; b < G; b++) {
+      const unsigned long long v = buf[(size_t)i * G + b];
+      ns[(size_t)i * G + b] = v ? ((double)v - (double)t0) * 1e6 / khz : -1.0;
+    }
+  return cnt < n_marks ? cnt : n_marks;
 }
 
 int dsl_layer_grid(const dsl_layer *L, int32_t *blocks, int32_t *threads) {

@@ -32,6 +32,7 @@ enum Mode : int { kModeDecode = 0, kModeAttn = 1, kModeMoe = 2 };
 // Split-K chunk (elements of K per task) of each linear; K / chunk partial sums.
 struct Plan {
   int kc_qkv, kc_qb, kc_oa, kc_ob, kc_sh13, kc_shd;
+  int kc_router;  // K chunk of a router task (a multiple of 128 dividing hidden)
 };
 
 // Per-width scratch (device pointers into one allocation).
@@ -48,7 +49,7 @@ struct Scratch {
   uint16_t *xin;           // bf16 input of layers after the first [M][h]
   uint16_t *hres;          // bf16 residual after attention [M][h]
   uint16_t *u;             // bf16 MoE input [M][h]
-  float *logits;           // [M][E]
+  float *logits;           // router partial logits [hidden / kc_router][M][E]
   float *p_sh;             // [nks][M][2*Is]
   uint16_t *zsh;           // bf16 shared SwiGLU output [M][Is]
   uint16_t *zr;            // bf16 routed SwiGLU output per (row, slot) pair [M*k][I]
@@ -79,6 +80,7 @@ struct Routing {
   float w[DSL_MAX_ROWS * 8];
   int pair[DSL_MAX_ROWS * 8];      // (row, slot) -> pair index, ordered by expert then row
   int pair_row[DSL_MAX_ROWS * 8];  // pair -> row
+  unsigned long long rows[128];    // rows that selected each expert (bit m)
   int cnt[128], start[128], list[128];
   int nd;
 };
@@ -107,7 +109,10 @@ __device__ __forceinline__ Ctx make_ctx() {
   const int t = tid();
   c.lane = t & 63;
   c.wave = t >> 6;
-  c.gw = bid() * kWavesPerBlock + c.wave;
+  // wave-major: consecutive task indices go to different blocks (compute units, and
+  // round-robin XCDs), so a stage with fewer tasks than waves still spreads its
+  // memory traffic over the whole chip
+  c.gw = c.wave * (int)gridDim.x + bid();
   c.nw = gridDim.x * kWavesPerBlock;
   return c;
 }
@@ -403,30 +408,50 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
 }
 
-// E contiguous float32 values: the sum over nks partial buffers (stride apart).
+// v[e] = sum over ks < nks (in ks order) of p[ks * stride + e]: the loads of up to B
+// partials are issued together, then added in order, so a stage does not wait a
+// round trip per partial.
 template <int E>
 __device__ __forceinline__ void load_sum_f32(const float *p, size_t stride, int nks, float v[E]) {
-  if constexpr (E >= 4) {
+  constexpr int B = E >= 32 ? 1 : (E >= 4 ? 32 / E : 8);
 #pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const float4 a = ld_f4(p + e);
-      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
-    }
-    for (int ks = 1; ks < nks; ks++) {
+  for (int e = 0; e < E; e++) v[e] = 0.f;
+  for (int k0 = 0; k0 < nks; k0 += B) {
+    float t[B][E];
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const float4 a = ld_f4(p + ks * stride + e);
-        v[e] += a.x; v[e + 1] += a.y; v[e + 2] += a.z; v[e + 3] += a.w;
+    for (int b = 0; b < B; b++) {
+      if (k0 + b < nks) {
+        const float *q = p + (size_t)(k0 + b) * stride;
+        if constexpr (E >= 4) {
+#pragma unroll
+          for (int e = 0; e < E; e += 4) {
+            const float4 a = ld_f4(q + e);
+            t[b][e] = a.x; t[b][e + 1] = a.y; t[b][e + 2] = a.z; t[b][e + 3] = a.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; e++) t[b][e] = ldg(q + e);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; e++) t[b][e] = 0.f;
       }
     }
-  } else {
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its adds
 #pragma unroll
-    for (int e = 0; e < E; e++) v[e] = ldg(p + e);
-    for (int ks = 1; ks < nks; ks++) {
+    for (int b = 0; b < B; b++)
+      if (k0 + b < nks) {
 #pragma unroll
-      for (int e = 0; e < E; e++) v[e] += ldg(p + ks * stride + e);
-    }
+        for (int e = 0; e < E; e++) v[e] = k0 + b == 0 ? t[b][e] : v[e] + t[b][e];
+      }
   }
+}
+
+// sum over ks < n (in ks order) of p[ks * stride], up to 8 loads in flight
+__device__ __forceinline__ float sum_strided(const float *p, size_t stride, int n) {
+  float v;
+  load_sum_f32<1>(p, stride, n, &v);
+  return v;
 }
 
 template <int E>
@@ -489,23 +514,5 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float lim) {
   u = fminf(fmaxf(u, -lim), lim);
   return g / (1.0f + expf(-g)) * u;
 }
-
-// Device task queue over task ids [0, T): a wave's first task is its global wave id
-// (no atomic), later tasks are claimed past the grid's first round with one atomic
-// per claim on the queue's counter, so a stage start does not serialize every wave on
-// one address.  `ctr` must be zero when the stage begins.
-struct TaskQueue {
-  unsigned *ctr;
-  int nw;
-  int next;  // this wave's next task id
-  __device__ __forceinline__ TaskQueue(unsigned *c, const Ctx &cx) : ctr(c), nw(cx.nw), next(cx.gw) {}
-  __device__ __forceinline__ int take(int lane) {
-    const int t = next;
-    unsigned c = 0;
-    if (lane == 0) c = __hip_atomic_fetch_add(gptr(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    next = nw + __shfl((int)c, 0, kWave);
-    return t;
-  }
-};
 
 }  // namespace dsl

@@ -138,12 +138,14 @@ def dsl_layer_set_trace(h, on: bool):
     _check(lib().dsl_layer_set_trace(h, 1 if on else 0))
 
 
-def dsl_layer_read_trace(h, n: int = 256) -> list:
-    buf = (ctypes.c_double * n)()
-    cnt = lib().dsl_layer_read_trace(h, buf, n)
+def dsl_layer_read_trace(h, n_marks: int = 256) -> np.ndarray:
+    """Stamps of the last traced launch: [marks, blocks] nanoseconds (-1 = none)."""
+    blocks, _ = dsl_layer_grid(h)
+    buf = np.zeros(n_marks * blocks, dtype=np.float64)
+    cnt = lib().dsl_layer_read_trace(h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n_marks)
     if cnt < 0:
         _check(cnt)
-    return [buf[i] for i in range(cnt)]
+    return buf[: cnt * blocks].reshape(cnt, blocks)
 
 
 def dsl_layer_destroy(h):
