@@ -470,82 +470,58 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
   }
 }
 
-// Routing of every live row, built by every block in its own LDS.  Wave w takes rows
-// w, w + 8, ...: lane l holds logits l and l + 64 (the router's partials summed in chunk
-// order, so every block gets the same values), top-k by k rounds of wave arg-max (ties
-// to the lower id, emitted in descending order), weights = softmax of the selected
-// logits.  Then per expert the set of rows that chose it, the distinct-expert list in
-// id order and the (row, slot) -> pair map ordered by expert, then by row.
-constexpr int kRowsPerWave = (DSL_MAX_ROWS + kWavesPerBlock - 1) / kWavesPerBlock;
-
-__device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R, bool all_live,
-                                              float *logits_tap) {
-  const int k = p.k, E = p.E, M = p.M, nc = p.h / p.pl.kc_router, lane = cx.lane, t0 = tid();
-  for (int e = t0; e < 128; e += kThreads) R.rows[e] = 0ull;
-  float a0[kRowsPerWave], a1[kRowsPerWave];
-  bool live[kRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; r++) {
-    const int m = cx.wave + r * kWavesPerBlock;
-    const int mc = m < M ? m : M - 1;
-    live[r] = m < M && (all_live || ldg(p.pos + mc) >= 0);
-    const float *lg = p.s.logits + (size_t)mc * E;
-    const size_t cs = (size_t)M * E;
-    const float s0 = m < M && lane < E ? sum_strided(lg + lane, cs, nc) : 0.f;
-    const float s1 = m < M && lane + 64 < E ? sum_strided(lg + lane + 64, cs, nc) : 0.f;
-    if (logits_tap && m < M) {
-      if (lane < E) stg(logits_tap + (size_t)m * E + lane, s0);
-      if (lane + 64 < E) stg(logits_tap + (size_t)m * E + lane + 64, s1);
-    }
-    a0[r] = lane < E ? s0 : -INFINITY;
-    a1[r] = lane + 64 < E ? s1 : -INFINITY;
+// Top-k of row m (one wave): the router's partial logits summed in chunk order, k rounds
+// of wave arg-max on (logit, lower id first) keys, so ties go to the lower id and the
+// selected ids come out in descending logit order; weights = softmax of the selected
+// logits.  Pad rows select nothing (ids -1, weights 0).
+__device__ __forceinline__ void topk_row(const Params &p, int m, bool live, int lane, float *logits_tap) {
+  const int k = p.k, E = p.E, M = p.M, nc = p.h / p.pl.kc_router;
+  const float *lg = p.s.logits + (size_t)m * E;
+  const size_t cs = (size_t)M * E;
+  const int l0 = lane < E ? lane : 0, l1 = lane + 64 < E ? lane + 64 : 0;
+  float a0 = sum_strided(lg + l0, cs, nc), a1 = sum_strided(lg + l1, cs, nc);
+  if (logits_tap) {
+    if (lane < E) stg(logits_tap + (size_t)m * E + lane, a0);
+    if (lane + 64 < E) stg(logits_tap + (size_t)m * E + lane + 64, a1);
   }
-  __syncthreads();
-  int myid[kRowsPerWave];
-  float myval[kRowsPerWave];
-  uint64_t k0[kRowsPerWave], k1[kRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; r++) {
-    myid[r] = -1;
-    myval[r] = -INFINITY;
-    k0[r] = amax_key(a0[r], lane);
-    k1[r] = amax_key(a1[r], lane + 64);
-  }
-  const int nrows = M > cx.wave ? (M - cx.wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
-  const uint64_t taken = 0ull;  // key of a removed entry (below every real key)
+  if (lane >= E) a0 = -INFINITY;
+  if (lane + 64 >= E) a1 = -INFINITY;
+  uint64_t k0 = amax_key(a0, lane), k1 = amax_key(a1, lane + 64);
+  int myid = -1;
+  float myval = -INFINITY;
   for (int j = 0; j < k; j++) {
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; r++) {
-      if (r < nrows) {
-        const uint64_t best = wave_max_key(k0[r] > k1[r] ? k0[r] : k1[r], lane);
-        if (lane == j) {
-          myid[r] = amax_key_index(best);
-          myval[r] = amax_key_value(best);
-        }
-        if (k0[r] == best) k0[r] = taken;
-        if (k1[r] == best) k1[r] = taken;
-      }
+    const uint64_t best = wave_max_key(k0 > k1 ? k0 : k1, lane);
+    if (lane == j) {
+      myid = amax_key_index(best);
+      myval = amax_key_value(best);
     }
+    k0 = k0 == best ? 0ull : k0;
+    k1 = k1 == best ? 0ull : k1;
   }
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; r++) {
-    const int m = cx.wave + r * kWavesPerBlock;
-    if (m >= M) break;
-    if (!live[r]) {
-      if (lane < k) {
-        R.ids[m * k + lane] = -1;
-        R.w[m * k + lane] = 0.f;
-      }
-      continue;
-    }
-    const float top = __shfl(myval[r], 0, kWave);
-    const float ev = lane < k ? expf(myval[r] - top) : 0.f;
-    const float sum = wave_sum(ev);
-    if (lane < k) {
-      R.ids[m * k + lane] = myid[r];
-      R.w[m * k + lane] = ev / sum;
-      atomicOr(&R.rows[myid[r]], 1ull << m);
-    }
+  const float top = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(myval), 0));
+  const float ev = lane < k ? expf(myval - top) : 0.f;
+  float sum = ev;
+  sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0xB1, 0xF, 0xF, false));   // quad xor 1
+  sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x4E, 0xF, 0xF, false));   // quad xor 2
+  sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x141, 0xF, 0xF, false));  // half-row mirror
+  if (lane < k) {
+    stg(p.s.tk_ids + (size_t)m * k + lane, live ? (int32_t)myid : (int32_t)-1);
+    stg(p.s.tk_w + (size_t)m * k + lane, live ? ev / sum : 0.f);
+  }
+}
+
+// Routing of the current layer in every block's LDS, from the selected ids and weights:
+// per expert the set of rows that chose it, the distinct-expert list in id order and
+// the (row, slot) -> pair map ordered by expert, then by row.
+__device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R) {
+  const int k = p.k, M = p.M, t0 = tid();
+  for (int e = t0; e < 128; e += kThreads) R.rows[e] = 0ull;
+  __syncthreads();
+  for (int t = t0; t < M * k; t += kThreads) {
+    const int id = ldg(p.s.tk_ids + t);
+    R.ids[t] = id;
+    R.w[t] = ldg(p.s.tk_w + t);
+    if (id >= 0) atomicOr(&R.rows[id], 1ull << (t / k));
   }
   __syncthreads();
   // counts, starts (exclusive scan in expert order) and the compacted expert list:
@@ -1118,8 +1094,15 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     SYNC();
     {
       STAGE(l);
-      build_routing(p, cx, R, moe_mode, bid() == 0 && last ? p.taps.logits : nullptr);
-      tr.mark();
+      // one wave per row selects its experts; every block takes part in the shared SwiGLU
+      if (cx.gw < p.M)
+        topk_row(p, cx.gw, moe_mode || ldg(p.pos + cx.gw) >= 0, cx.lane, last ? p.taps.logits : nullptr);
+      st_shared_swiglu(p, moe_mode);
+    }
+    SYNC();
+    {
+      STAGE(l);
+      build_routing(p, cx, R);
       if (bid() == 0 && p.taps.layer_ids)
         for (int t = tid(); t < p.M * p.k; t += kThreads)
           stg(p.taps.layer_ids + (size_t)l * p.M * p.k + t, R.ids[t]);
@@ -1129,10 +1112,6 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           if (p.taps.topk_w) stg(p.taps.topk_w + t, R.w[t]);
         }
       }
-    }
-    {
-      STAGE(l);
-      st_shared_swiglu(p, moe_mode);
     }
     tr.mark();
     {
@@ -1264,6 +1243,8 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   s->hres = (uint16_t *)take(m * h * 2);
   s->u = (uint16_t *)take(m * h * 2);
   s->logits = (float *)take((h / pl.kc_router) * m * E * 4);
+  s->tk_ids = (int32_t *)take(m * k * 4);
+  s->tk_w = (float *)take(m * k * 4);
   s->p_sh = (float *)take((h / pl.kc_sh13) * m * 2 * Is * 4);
   s->zsh = (uint16_t *)take(m * Is * 2);
   s->zr = (uint16_t *)take(m * k * I * 2);
