@@ -761,13 +761,13 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
   }
 }
 
-// Down projection of one expert for its CE pairs over a tile of 16 output rows
-template <int CE, int Q>
+// Down projection of one expert for its CE pairs over a tile of NR output rows
+template <int CE, int Q, int NR>
 __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile,
                                                  int lane, uint8_t *sl) {
   constexpr int NB = 64 * Q;
   constexpr int G = 16 / CE;
-  constexpr int NR = 16;
+  static_assert(NR % 16 == 0 && NR * NB <= 4096, "tile rows and their staged scales");
   const int h = p.h, I = p.I;
   const size_t row_bytes = (size_t)I >> 1;
   const uint8_t *W = w.ex_wd + (size_t)e * h * row_bytes;
@@ -777,13 +777,14 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   for (int m = 0; m < CE; m++) rows[m] = p.s.zr + (size_t)(p0 + (m < ce ? m : 0)) * I;
   uint32_t xv[Q][CE][16];
   valu_load_x<CE, Q>(rows, lane, xv);
-  valu_stage_scales<Q>(S + (size_t)(tile * 16) * NB, sl, lane);
+#pragma unroll
+  for (int b = 0; b < NR / 16; b++) valu_stage_scales<Q>(S + (size_t)(tile * NR + 16 * b) * NB, sl + 16 * NB * b, lane);
   constexpr int DEPTH = kValuDepth / Q;
   v4u ring[DEPTH][Q];
 #pragma unroll
   for (int r = 0; r < DEPTH; r++)
 #pragma unroll
-    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)(tile * 16 + r) * row_bytes + 16 * (lane + 64 * q));
+    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)(tile * NR + r) * row_bytes + 16 * (lane + 64 * q));
   float acc[16];
 #pragma unroll
   for (int r = 0; r < NR; r++) {
@@ -798,7 +799,7 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
     if (r + DEPTH < NR) {
 #pragma unroll
       for (int q = 0; q < Q; q++)
-        ring[r % DEPTH][q] = ld16(W + (size_t)(tile * 16 + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
+        ring[r % DEPTH][q] = ld16(W + (size_t)(tile * NR + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
     }
 #pragma unroll
     for (int q = 0; q < Q; q++) {
@@ -808,7 +809,7 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
     if (rr == G - 1) {
       const float tot = wave_transpose_sum<16>(acc, lane);
       const int j = lane >> 2;  // value (row, pair) = (j / CE, j % CE)
-      if ((lane & 3) == 0 && j % CE < ce) stg(p.s.y + (size_t)(p0 + j % CE) * h + tile * 16 + gi * G + j / CE, tot);
+      if ((lane & 3) == 0 && j % CE < ce) stg(p.s.y + (size_t)(p0 + j % CE) * h + tile * NR + gi * G + j / CE, tot);
     }
   }
 }
@@ -846,26 +847,35 @@ __device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const ds
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
   for (int t = cx.gw; t < TS; t += cx.nw)
     linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
-  const int tiles_n = p.h >> 4;
+  // tiles of TR output rows (TR / 16 tasks on the matrix-core path)
+  constexpr int TR = 16;
+  const int tiles_n = p.h / TR;
   const int T = R.nd * tiles_n;
   const int qv = p.I == 2048 ? 1 : p.I == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
-    const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
+    // wave-uniform: keep them (and the addresses built on them) in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(R.list[q]);
+    const int ce = __builtin_amdgcn_readfirstlane(R.cnt[e]), p0 = __builtin_amdgcn_readfirstlane(R.start[e]);
     const int ncg = (ce + 15) >> 4;
     if (qv == 1 && ce <= 4) {
-      if (ce == 1) routed_down_valu<1, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
-      else if (ce == 2) routed_down_valu<2, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
-      else routed_down_valu<4, 1>(p, w, e, p0, ce, tile, cx.lane, sl);
+      if (ce == 1) routed_down_valu<1, 1, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else if (ce == 2) routed_down_valu<2, 1, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else routed_down_valu<4, 1, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
     } else if (qv == 2 && ce <= 2) {
-      if (ce == 1) routed_down_valu<1, 2>(p, w, e, p0, ce, tile, cx.lane, sl);
-      else routed_down_valu<2, 2>(p, w, e, p0, ce, tile, cx.lane, sl);
-    } else if (ncg == 1)
-      routed_down_task<1>(p, w, e, p0, ce, tile, cx.lane);
-    else if (ncg == 2)
-      routed_down_task<2>(p, w, e, p0, ce, tile, cx.lane);
-    else
-      routed_down_task<3>(p, w, e, p0, ce, tile, cx.lane);
+      if (ce == 1) routed_down_valu<1, 2, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
+      else routed_down_valu<2, 2, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
+    } else {
+      for (int sub = 0; sub < TR / 16; sub++) {
+        const int t16 = tile * (TR / 16) + sub;
+        if (ncg == 1)
+          routed_down_task<1>(p, w, e, p0, ce, t16, cx.lane);
+        else if (ncg == 2)
+          routed_down_task<2>(p, w, e, p0, ce, t16, cx.lane);
+        else
+          routed_down_task<3>(p, w, e, p0, ce, t16, cx.lane);
+      }
+    }
   }
 }
 
