@@ -146,6 +146,50 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources and the header the library is built from: a stored
+    traffic measurement is used only for the kernel it was taken on."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for rel in ("moe_transformer_layer_amd/csrc/dsl_kernel.hip", "moe_transformer_layer_amd/csrc/dsl_stages.h",
+                "moe_transformer_layer_amd/csrc/dsl_device.h", "include/dsl.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dsl_layer_kernel_hbm_traffic_decode_m6.txt")
+
+
+def measured_traffic():
+    """HBM bytes per M=6 launch from the counter summary in profiles/ (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy's reading), or None when that summary was taken on
+    other kernel sources."""
+    try:
+        vals = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+        if vals.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return float(vals["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calib_copy(mb: int, reps: int = 10):
+    """A plain device copy of `mb` MiB, for scaling the HBM byte counters."""
+    import torch
+    n = mb << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,7 +198,12 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="distinct weight copies rotated for cold weights")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only-m6", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.calib_copy:
+        calib_copy(args.calib_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs one GPU only (asked for {args.gpus}): this library has no multi-GPU path; "
               "tensor-parallel sharding is a design note, not built", file=sys.stderr)
@@ -195,7 +244,7 @@ def main():
                                "q/o rank 1024, window 128, top-6 of 128 MXFP4 experts (inter 2048), FP8 shared 2048, "
                                "cold weights", "rows": 6, "seq_context": "1k-64k paged, block 128"},
         "roofline": {"bound": "hbm", "achieved": round(m6["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(m6["frac"], 4), "traffic": None,
+                     "frac": round(m6["frac"], 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": m6["bytes"]["total"], "kernel_us_mean": round(m6["us_kernel_mean"], 2)},
         "m6": m6,
         "m48": m48,
