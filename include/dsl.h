@@ -30,6 +30,11 @@
  *     at most 48 rows).  Each width gets its own scratch at its first step
  *     ("Design": a scratch per step width); dsl_layer_reserve() allocates it
  *     ahead of time (call it before capturing a step into a HIP graph).
+ *   - A step is one plain launch of one block per compute unit (all a unit holds of
+ *     this kernel), and its stages meet at grid barriers, so it needs every block
+ *     resident at once: give it the device.  A concurrent kernel that holds compute
+ *     units only delays it; one that holds them past the barrier's bounded wait
+ *     (about half a second) makes the step report DSL_EDEVICE instead of hanging.
  *   - positions[r] = -1 marks a pad row: no KV write, ids -1, weights 0 and zero
  *     rows in every output ("Test Plan": the kernels skip pad rows, whose slot
  *     is -1).  Rows of one request must have distinct positions.
@@ -46,7 +51,7 @@ extern "C" {
 #define DSL_OK 0
 #define DSL_EINVAL (-1)       /* a null pointer, a bad stride, a size out of range  */
 #define DSL_EUNSUPPORTED (-2) /* dims or widths the kernels do not cover; not gfx950;
-                                 fewer CUs than one co-resident grid needs        */
+                                 the kernel's block does not fit a compute unit  */
 #define DSL_ENOMEM (-3)       /* device allocation failed                            */
 #define DSL_EHIP (-4)         /* a HIP runtime call failed (message has the code)    */
 #define DSL_EDEVICE (-5)      /* dsl_layer_health: a device-side fault was recorded  */
@@ -140,8 +145,8 @@ typedef struct {
 
 typedef struct dsl_layer dsl_layer;
 
-/* Validate dims, query the current device (must be gfx950 with enough CUs for the
- * co-resident grid), copy the n_layers weight descriptors (not the weights) and
+/* Validate dims, query the current device (must be gfx950, and one block of the
+ * layer kernel must fit on a compute unit), copy the n_layers weight descriptors (not the weights) and
  * allocate the sync buffer.  weights points to dims->n_layers descriptors.
  * On success *out receives the handle.  Errors: DSL_EINVAL, DSL_EUNSUPPORTED,
  * DSL_ENOMEM, DSL_EHIP. */

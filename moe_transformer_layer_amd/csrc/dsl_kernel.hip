@@ -1,13 +1,14 @@
-// The decode layer as one persistent cooperative launch on gfx950, and the host
-// runtime behind the C ABI of include/dsl.h.
+// The decode layer as one persistent launch (one block per compute unit) on gfx950,
+// and the host runtime behind the C ABI of include/dsl.h.
 //
 // One launch runs, per layer, the stages of "Mono decode layer for
 // DeepSeek-V4.1-Flash on MI355X" (vLLM PR 60397), Purpose, launch table (K1 and
 // K2 without the tensor-parallel all-reduces), with a grid barrier between
 // dependent stages.  Three draft layers chain inside the same launch ("Mono
-// decode for the DSpark draft layers", vLLM PR 62131, Details).  Routed-expert
-// work is claimed from a device task queue (atomic counters in the handle's sync
-// buffer), everything else is split statically over the grid's waves.
+// decode for the DSpark draft layers", vLLM PR 62131, Details).  Every stage's
+// tasks are split statically over the grid's waves in wave-major order (task t to
+// wave t mod waves, consecutive tasks on different compute units); the routed
+// experts' tasks follow the routing table every block builds from the top-k.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -1313,9 +1314,6 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   HIPCHK(hipGetDeviceProperties(&prop, dev));
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(DSL_EUNSUPPORTED, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
-  int coop = 0;
-  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
-  if (!coop) return fail(DSL_EUNSUPPORTED, "device %d does not support cooperative launches", dev);
   int bpc = 0;
   HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel, kThreads, 0));
   if (bpc < 1) return fail(DSL_EUNSUPPORTED, "the layer kernel cannot be resident on a compute unit");
@@ -1415,8 +1413,10 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   p.trace = L->trace;
   void *args[] = {&p};
   HIPCHK(hipSetDevice(L->dev));
-  HIPCHK(hipLaunchCooperativeKernel((const void *)dsl_layer_kernel, dim3(L->grid), dim3(kThreads), args, 0,
-                                    (hipStream_t)stream));
+  // A plain launch: one block per compute unit is all that fits (the occupancy check at
+  // build), so on a device this launch has to itself every block is resident at once.
+  // The cooperative launch path costs ~18 us more per launch on this device.
+  HIPCHK(hipLaunchKernel((const void *)dsl_layer_kernel, dim3(L->grid), dim3(kThreads), args, 0, (hipStream_t)stream));
   return 0;
 }
 
