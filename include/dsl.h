@@ -64,8 +64,9 @@ extern "C" {
  * n_heads*head_dim positive multiples of 128 (the kernels stream K in steps of
  * 128; the shared expert has 128x128 scale blocks); head_dim in {64, 128, 256,
  * 512}; 1 <= n_experts <= 128; 1 <= top_k <= min(8, n_experts);
- * 1 <= max_rows <= 48; 1 <= n_layers <= DSL_MAX_LAYERS; window >= 1;
- * swa_width >= 0; kv_block >= 1.  Other values: DSL_EUNSUPPORTED or DSL_EINVAL. */
+ * 1 <= max_rows <= 48; 1 <= n_layers <= DSL_MAX_LAYERS; 1 <= window <= 256;
+ * 0 <= swa_width <= 256 (a row's keys are split over at most 8 waves of 32 keys);
+ * kv_block >= 1.  Other values: DSL_EUNSUPPORTED or DSL_EINVAL. */
 typedef struct {
   int32_t hidden, n_heads, head_dim, q_rank, o_rank;
   int32_t window;      /* causal sliding window W; a row at position p sees

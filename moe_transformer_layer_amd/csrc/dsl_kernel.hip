@@ -26,12 +26,45 @@ namespace dsl {
 // Row stages run one row per block: every thread holds E contiguous values, issues
 // all of its loads at once, and block reductions combine the rows' sums.
 
-// RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values)
+__device__ __forceinline__ int64_t slot_of(const Params &p, const dsl_kv &kv, int req, int t);
+__device__ __forceinline__ int64_t record_off(const Params &p, const dsl_kv &kv, int64_t slot);
+
+// The cache byte offset of every key of row m (-1 past the row's keys or for a pad
+// row): the causal window [max(0, p - W + 1), p] through the block table, or the row of
+// the caller's slot table.  Written for the attention stage, so that it reaches a record
+// in one load.
+__device__ __forceinline__ void key_offsets_row(const Params &p, const dsl_kv &kv, int m) {
+  const int keys = p.swa > 0 ? p.swa : p.W;
+  const int pos = ldg(p.pos + m);
+  const int req = ldg(kv.row_req + m);
+  const int lo = pos - p.W + 1 < 0 ? 0 : pos - p.W + 1;
+  for (int j = tid(); j < keys; j += kThreads) {
+    int64_t off = -1;
+    if (pos >= 0) {
+      if (p.swa > 0) {
+        const int64_t slot = ldg(kv.key_table + (size_t)m * p.swa + j);
+        if (slot >= 0) off = record_off(p, kv, slot);
+      } else if (lo + j <= pos) {
+        off = record_off(p, kv, slot_of(p, kv, req, lo + j));
+      }
+    }
+    stg(p.s.keyoff + (size_t)m * keys + j, off);
+  }
+}
+
+// RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values); the
+// block of row m also resolves the row's key records.
 template <int E>
-__device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, float *red) {
+__device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const dsl_kv &kv,
+                                               const uint16_t *xin, float *red) {
   const int n = p.h, k = tid() * E;
   const bool act = k < n;
+  // the key records of row m are resolved by block M + m (or by block m itself when the
+  // grid has fewer than 2 M blocks), in parallel with the norm
+  const bool split = (int)gridDim.x >= 2 * p.M;
+  if (split && bid() >= p.M && bid() < 2 * p.M) key_offsets_row(p, kv, bid() - p.M);
   for (int m = bid(); m < p.M; m += gridDim.x) {
+    if (!split) key_offsets_row(p, kv, m);
     float v[E];
     if (act)
       load_bf16<E>(xin + (size_t)m * n + k, v);
@@ -59,6 +92,17 @@ __device__ __forceinline__ uint8_t *record_ptr(const Params &p, const dsl_kv &kv
     return nullptr;
   }
   return kv.base + blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
+}
+
+// Byte offset of a slot's record in the cache, or -1 (with a recorded fault) if the slot
+// is outside the cache view.
+__device__ __forceinline__ int64_t record_off(const Params &p, const dsl_kv &kv, int64_t slot) {
+  const int64_t blk = slot / p.B;
+  if (slot < 0 || blk >= kv.n_blocks) {
+    __hip_atomic_fetch_or(gptr(&p.sync->health), (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return -1;
+  }
+  return blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
 }
 
 // Slot of token position t of request req through the block table, or -1.
@@ -141,6 +185,26 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
                                             uint8_t *tmp) {
   const int eq = row_elems(p.qr), ekv = row_elems(p.D);
+  // q of row m on block m, kv of row m on block M + m (both on block m when the grid has
+  // fewer than 2 M blocks)
+  if ((int)gridDim.x >= 2 * p.M) {
+    const int b = bid();
+    if (b < p.M) {
+      switch (eq) {
+        case 1: qpost_row<1>(p, w, b, red); break;
+        case 2: qpost_row<2>(p, w, b, red); break;
+        case 4: qpost_row<4>(p, w, b, red); break;
+        case 8: qpost_row<8>(p, w, b, red); break;
+        default: qpost_row<16>(p, w, b, red); break;
+      }
+    } else if (b < 2 * p.M) {
+      switch (ekv) {
+        case 1: kvpost_row<1>(p, w, kv, b - p.M, red, tmp); break;
+        default: kvpost_row<2>(p, w, kv, b - p.M, red, tmp); break;
+      }
+    }
+    return;
+  }
   for (int m = bid(); m < p.M; m += gridDim.x) {
     switch (eq) {
       case 1: qpost_row<1>(p, w, m, red); break;
@@ -185,154 +249,133 @@ __device__ __forceinline__ uint64_t load_codes(const uint8_t *p) {
 }
 
 // One (row, head, split): scores q . k / sqrt(D) over up to 32 keys of the row's key set,
-// with k = v = scale * e4m3(codes) of the record; partial max, sum of exponentials and
-// exponential-weighted sum of values.  Lane j < 32 resolves key j's record; then every
-// lane loads its V dims of all 32 keys at once.  Lane l holds dims [V*l, V*l + V).
+// with k = v = scale * e4m3(codes) of the record; returns the partial max, the sum of
+// exponentials and (lane l: dims [V l, V l + V)) the exponential-weighted sum of values.
+// Lane j < 32 reads key j's record offset and scale; each key's offset reaches the wave
+// as a scalar (readlane), every lane loads its V dims of the 32 keys at once and keeps
+// them for the value pass, and the 32 dot products are summed across the wave by the
+// transposing butterfly, 16 keys at a time.
 template <int V>
-__device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane) {
+__device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane,
+                                          float &mx_out, float &l_out, float (&o)[V]) {
   const int D = p.D, H = p.H;
-  const int pos = ldg(p.pos + m);
-  const size_t item = ((size_t)m * H + hh) * p.S + sp;
-  int nk, lo = 0;
-  if (p.swa > 0) {
-    nk = p.swa;
-  } else {
-    lo = pos - p.W + 1 < 0 ? 0 : pos - p.W + 1;
-    nk = pos - lo + 1;
-  }
+  const int keys = p.swa > 0 ? p.swa : p.W;
   const int j0 = sp * kSplitKeys;
-  // lane j < 32: the record of key j0 + j (or null)
-  const uint8_t *myrec = nullptr;
-  if (lane < kSplitKeys && j0 + lane < nk) {
-    int64_t slot;
-    if (p.swa > 0) {
-      slot = ldg(kv.key_table + (size_t)m * p.swa + j0 + lane);
-      myrec = slot < 0 ? nullptr : record_ptr(p, kv, slot);
-    } else {
-      myrec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), lo + j0 + lane));
-    }
-  }
-  const float mysc = myrec ? ldg(reinterpret_cast<const float *>(myrec + D)) : 0.f;
+  int64_t myoff = -1;
+  if (lane < kSplitKeys && j0 + lane < keys) myoff = ldg(p.s.keyoff + (size_t)m * keys + j0 + lane);
+  const float mysc = myoff >= 0 ? ldg(reinterpret_cast<const float *>(kv.base + myoff + D)) : 0.f;
   const int nks = p.qr / p.pl.kc_qb;
   const size_t qstride = (size_t)p.M * H * D;
   const float *qp = p.s.p_q + (size_t)m * H * D + (size_t)hh * D + lane * V;
   float q[V];
   load_sum_f32<V>(qp, qstride, nks, q);
-  const uint64_t recbits = reinterpret_cast<uint64_t>(myrec);
-  constexpr int HALF = kSplitKeys / 2;
-  // scores, 16 keys at a time: every lane loads its V dims of the 16 keys at once
-  float my = -INFINITY;
+  const uint32_t olo = (uint32_t)(uint64_t)myoff, ohi = (uint32_t)((uint64_t)myoff >> 32);
+  // key j's record offset, as a scalar
+  auto key_off = [&](int j) -> int64_t {
+    return (int64_t)(((uint64_t)__builtin_amdgcn_readlane(ohi, j) << 32) | __builtin_amdgcn_readlane(olo, j));
+  };
+  float sc[2];
 #pragma unroll
-  for (int h0 = 0; h0 < kSplitKeys; h0 += HALF) {
-    uint64_t codes[HALF];
+  for (int hf = 0; hf < 2; hf++) {
+    uint64_t codes[16];
 #pragma unroll
-    for (int j = 0; j < HALF; j++) {
-      const uint64_t rb = ((uint64_t)__shfl((unsigned)(recbits >> 32), h0 + j, kWave) << 32) |
-                          (uint64_t)__shfl((unsigned)recbits, h0 + j, kWave);
-      codes[j] = rb ? load_codes<V>(reinterpret_cast<const uint8_t *>(rb) + lane * V) : 0ull;
+    for (int j = 0; j < 16; j++) {
+      const int64_t off = key_off(16 * hf + j);
+      codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
     }
+    float d[16];
 #pragma unroll
-    for (int j = 0; j < HALF; j++) {
+    for (int j = 0; j < 16; j++) {
       float c[V];
       decode_codes<V>(codes[j], c);
-      float d = 0.f;
+      float a = 0.f;
 #pragma unroll
-      for (int v = 0; v < V; v++) d += q[v] * c[v];
-      d = wave_sum(d);
-      if (lane == h0 + j) my = myrec ? d * mysc * p.attn_scale : -INFINITY;
+      for (int v = 0; v < V; v++) a += q[v] * c[v];
+      d[j] = a;
     }
+    sc[hf] = wave_transpose_sum<16>(d, lane);  // lane L: key 16 hf + (L >> 2)
   }
+  // lane j < 32: the score of key j
+  const float s0 = __shfl(sc[0], 4 * (lane & 15), kWave), s1 = __shfl(sc[1], 4 * (lane & 15), kWave);
+  const float my = myoff >= 0 ? (lane < 16 ? s0 : s1) * mysc * p.attn_scale : -INFINITY;
   const float mx = wave_max(my);
   const float pj = my == -INFINITY ? 0.f : expf(my - mx);
   const float l = wave_sum(pj);
   const float f = pj * mysc;
-  // output: the same records again (now cache hits), weighted by exp(score - max) * scale
-  float o[V];
+  // values: the same records again (cache hits), weighted by exp(score - max) * scale
 #pragma unroll
   for (int v = 0; v < V; v++) o[v] = 0.f;
 #pragma unroll
-  for (int h0 = 0; h0 < kSplitKeys; h0 += HALF) {
-    uint64_t codes[HALF];
+  for (int hf = 0; hf < 2; hf++) {
+    uint64_t codes[16];
 #pragma unroll
-    for (int j = 0; j < HALF; j++) {
-      const uint64_t rb = ((uint64_t)__shfl((unsigned)(recbits >> 32), h0 + j, kWave) << 32) |
-                          (uint64_t)__shfl((unsigned)recbits, h0 + j, kWave);
-      codes[j] = rb ? load_codes<V>(reinterpret_cast<const uint8_t *>(rb) + lane * V) : 0ull;
+    for (int j = 0; j < 16; j++) {
+      const int64_t off = key_off(16 * hf + j);
+      codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
     }
 #pragma unroll
-    for (int j = 0; j < HALF; j++) {
-      const float fj = __shfl(f, h0 + j, kWave);
+    for (int j = 0; j < 16; j++) {
+      const float fj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), 16 * hf + j));
       float c[V];
       decode_codes<V>(codes[j], c);
 #pragma unroll
       for (int v = 0; v < V; v++) o[v] += fj * c[v];
     }
   }
-  float *o_out = p.s.att_o + item * D + lane * V;
-  if constexpr (V >= 4) {
-#pragma unroll
-    for (int v = 0; v < V; v += 4) st_f4(o_out + v, make_float4(o[v], o[v + 1], o[v + 2], o[v + 3]));
-  } else {
-#pragma unroll
-    for (int v = 0; v < V; v++) stg(o_out + v, o[v]);
-  }
-  if (lane == 0) st_f2(p.s.att_ml + item * 2, make_float2(mx, l));
+  mx_out = mx;
+  l_out = l;
 }
 
+// Attention and the log-sum-exp combine in one stage: a block takes P = 8 / S (row, head)
+// items at a time, one wave per split; the splits' partials meet in LDS (lds: 8 D + 16
+// floats), where one wave per item combines them, quantizes the output to MXFP8 (a
+// 32-block spans 32 / V lanes) and stores it.  Pad rows give zeros.
 template <int V>
-__device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv) {
-  const int T = p.M * p.H * p.S;
-  for (int t = cx.gw; t < T; t += cx.nw) {
-    const int m = t / (p.H * p.S), rem = t - m * p.H * p.S;
-    const int hh = rem / p.S, sp = rem - hh * p.S;
-    if (ldg(p.pos + m) < 0) continue;
-    attn_item<V>(p, kv, m, hh, sp, cx.lane);
-  }
-}
-
-// Log-sum-exp combine of the splits of one (row, head), then MXFP8 of the output
-// (32-blocks span 32/V lanes).  Pad rows give zeros.
-template <int V>
-__device__ __forceinline__ void st_combine_v(const Params &p, const Ctx &cx) {
-  constexpr int SMAX = 8;
-  const int T = p.M * p.H, D = p.D, S = p.S;
-  for (int t = cx.gw; t < T; t += cx.nw) {
-    const int m = t / p.H, hh = t - m * p.H;
-    float o[V];
+__device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds) {
+  const int S = p.S, P = kWavesPerBlock / S, D = p.D;
+  const int T = p.M * p.H;
+  const int w = cx.wave, lane = cx.lane, i = w / S, sp = w - i * S;
+  float *lo_ = lds, *lml = lds + kWavesPerBlock * D;
+  for (int t0 = bid() * P; t0 < T; t0 += gridDim.x * P) {
+    const int t = t0 + i;
+    if (i < P && t < T) {
+      const int m = t / p.H, hh = t - m * p.H;
+      float mx = -INFINITY, l = 0.f, o[V];
 #pragma unroll
-    for (int v = 0; v < V; v++) o[v] = 0.f;
-    if (ldg(p.pos + m) >= 0) {
-      const size_t item0 = ((size_t)m * p.H + hh) * S;
-      float ms[SMAX], ls[SMAX], os[SMAX][V];
+      for (int v = 0; v < V; v++) o[v] = 0.f;
+      if (ldg(p.pos + m) >= 0) attn_item<V>(p, kv, m, hh, sp, lane, mx, l, o);
 #pragma unroll
-      for (int s = 0; s < SMAX; s++) {
-        const int sc = s < S ? s : S - 1;
-        const float2 ml = ld_f2(p.s.att_ml + (item0 + sc) * 2);
-        ms[s] = s < S ? ml.x : -INFINITY;
-        ls[s] = s < S ? ml.y : 0.f;
-        const float *op = p.s.att_o + (item0 + sc) * D + cx.lane * V;
-#pragma unroll
-        for (int v = 0; v < V; v++) os[s][v] = ldg(op + v);
+      for (int v = 0; v < V; v++) lo_[w * D + lane * V + v] = o[v];
+      if (lane == 0) {
+        lml[2 * w] = mx;
+        lml[2 * w + 1] = l;
       }
+    }
+    __syncthreads();
+    if (w < P && t0 + w < T) {
+      const int tt = t0 + w, m = tt / p.H, hh = tt - m * p.H;
+      float o[V];
+#pragma unroll
+      for (int v = 0; v < V; v++) o[v] = 0.f;
       float mx = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < SMAX; s++) mx = fmaxf(mx, ms[s]);
+      for (int s = 0; s < S; s++) mx = fmaxf(mx, lml[2 * (w * S + s)]);
       float L = 0.f;
+      for (int s = 0; s < S; s++) {
+        const float ls = lml[2 * (w * S + s) + 1];
+        if (!(ls > 0.f)) continue;
+        const float e = expf(lml[2 * (w * S + s)] - mx);
+        L += ls * e;
 #pragma unroll
-      for (int s = 0; s < SMAX; s++) {
-        if (!(ls[s] > 0.f)) continue;
-        const float e = expf(ms[s] - mx);
-        L += ls[s] * e;
-#pragma unroll
-        for (int v = 0; v < V; v++) o[v] += os[s][v] * e;
+        for (int v = 0; v < V; v++) o[v] += lo_[(w * S + s) * D + lane * V + v] * e;
       }
       if (L > 0.f) {
 #pragma unroll
         for (int v = 0; v < V; v++) o[v] = o[v] / L;
       }
+      mx_quant_dequant<V>(o);
+      store_bf16<V>(p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + lane * V, o);
     }
-    mx_quant_dequant<V>(o);
-    store_bf16<V>(p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + cx.lane * V, o);
+    __syncthreads();
   }
 }
 
@@ -692,7 +735,7 @@ __device__ __forceinline__ void valu_stage_scales(const uint8_t *src, uint8_t *d
   }
 }
 
-constexpr int kValuDepth = 8;  // weight rows in flight per wave
+constexpr int kValuDepth = 16;  // weight rows in flight per wave
 
 // Gate/up of one expert for its CE <= 2 rows over a tile of 16 gate and 16 up rows,
 // SwiGLU in the epilogue.  Rows are taken in groups of G = 16 / CE (half gate, half up)
@@ -1015,13 +1058,23 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     if (!moe_mode) {
       {
         STAGE(l);
+        // blocks this stage leaves idle fetch the next two linears' weights
+        const int busy = 2 * p.M;
+        if (bid() >= busy) {
+          const int nwk = ((int)gridDim.x - busy) * kWavesPerBlock, wk = (bid() - busy) * kWavesPerBlock + cx.wave;
+          void *pf = wave_lds[cx.wave];
+          prefetch_share(w.wqkv, (size_t)(p.qr + p.D) * p.h, wk, nwk, cx.lane, pf);
+          prefetch_share(w.wqkv_s, (size_t)((p.qr + p.D) / 32) * (p.h / 32), wk, nwk, cx.lane, pf);
+          prefetch_share(w.wq_b, (size_t)p.H * p.D * p.qr, wk, nwk, cx.lane, pf);
+          prefetch_share(w.wq_b_s, (size_t)(p.H * p.D / 32) * (p.qr / 32), wk, nwk, cx.lane, pf);
+        }
         const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
-          case 1: st_attn_norm_e<1>(p, w, xin, red); break;
-          case 2: st_attn_norm_e<2>(p, w, xin, red); break;
-          case 4: st_attn_norm_e<4>(p, w, xin, red); break;
-          case 8: st_attn_norm_e<8>(p, w, xin, red); break;
-          default: st_attn_norm_e<16>(p, w, xin, red); break;
+          case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
+          case 2: st_attn_norm_e<2>(p, w, kv, xin, red); break;
+          case 4: st_attn_norm_e<4>(p, w, kv, xin, red); break;
+          case 8: st_attn_norm_e<8>(p, w, kv, xin, red); break;
+          default: st_attn_norm_e<16>(p, w, kv, xin, red); break;
         }
       }
       SYNC();
@@ -1042,21 +1095,31 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       SYNC();
       {
         STAGE(l);
-        switch (p.D) {
-          case 64: st_attention_v<1>(p, cx, kv); break;
-          case 128: st_attention_v<2>(p, cx, kv); break;
-          case 256: st_attention_v<4>(p, cx, kv); break;
-          default: st_attention_v<8>(p, cx, kv); break;
+        // blocks the attention leaves idle fetch the weights of wo_a, wo_b, the router and
+        // the shared expert
+        const int per_block = kWavesPerBlock / p.S;
+        const int busy = (p.M * p.H + per_block - 1) / per_block;
+        if (bid() >= busy && mode != kModeMoe) {
+          const int nwk = ((int)gridDim.x - busy) * kWavesPerBlock, wk = (bid() - busy) * kWavesPerBlock + cx.wave;
+          void *pf = wave_lds[cx.wave];
+          prefetch_share(w.wo_a, (size_t)p.orr * p.H * p.D, wk, nwk, cx.lane, pf);
+          prefetch_share(w.wo_a_s, (size_t)(p.orr / 32) * (p.H * p.D / 32), wk, nwk, cx.lane, pf);
+          prefetch_share(w.wo_b, (size_t)p.h * p.orr, wk, nwk, cx.lane, pf);
+          prefetch_share(w.wo_b_s, (size_t)(p.h / 32) * (p.orr / 32), wk, nwk, cx.lane, pf);
+          if (mode == kModeDecode) {
+            prefetch_share(w.w_router, (size_t)p.E * p.h * 4, wk, nwk, cx.lane, pf);
+            prefetch_share(w.sh_w13, (size_t)2 * p.Is * p.h, wk, nwk, cx.lane, pf);
+            prefetch_share(w.sh_w13_s, (size_t)(2 * p.Is / 128) * (p.h / 128) * 4, wk, nwk, cx.lane, pf);
+            prefetch_share(w.sh_wd, (size_t)p.h * p.Is, wk, nwk, cx.lane, pf);
+            prefetch_share(w.sh_wd_s, (size_t)(p.h / 128) * (p.Is / 128) * 4, wk, nwk, cx.lane, pf);
+          }
         }
-      }
-      SYNC();
-      {
-        STAGE(l);
+        float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
         switch (p.D) {
-          case 64: st_combine_v<1>(p, cx); break;
-          case 128: st_combine_v<2>(p, cx); break;
-          case 256: st_combine_v<4>(p, cx); break;
-          default: st_combine_v<8>(p, cx); break;
+          case 64: st_attention_v<1>(p, cx, kv, lds); break;
+          case 128: st_attention_v<2>(p, cx, kv, lds); break;
+          case 256: st_attention_v<4>(p, cx, kv, lds); break;
+          default: st_attention_v<8>(p, cx, kv, lds); break;
         }
       }
       SYNC();
@@ -1215,6 +1278,9 @@ static int validate_dims(const dsl_dims *d) {
     return fail(DSL_EUNSUPPORTED, "top_k %d outside 1..min(8, n_experts)", d->top_k);
   if (d->window < 1) return fail(DSL_EINVAL, "window %d < 1", d->window);
   if (d->swa_width < 0) return fail(DSL_EINVAL, "swa_width %d < 0", d->swa_width);
+  if (d->window > 8 * kSplitKeys || d->swa_width > 8 * kSplitKeys)
+    return fail(DSL_EUNSUPPORTED, "window %d / swa_width %d: at most %d keys per row (8 splits of %d)", d->window,
+                d->swa_width, 8 * kSplitKeys, kSplitKeys);
   if (d->kv_block < 1) return fail(DSL_EINVAL, "kv_block %d < 1", d->kv_block);
   if (!(d->norm_eps >= 0.f) || !(d->swiglu_limit > 0.f))
     return fail(DSL_EINVAL, "norm_eps must be >= 0 and swiglu_limit > 0");
@@ -1244,8 +1310,8 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   s->p_qkv = (float *)take((h / pl.kc_qkv) * m * (qr + D) * 4);
   s->qb = (uint16_t *)take(m * qr * 2);
   s->p_q = (float *)take((qr / pl.kc_qb) * m * HD * 4);
-  s->att_o = (float *)take(m * d.n_heads * S * D * 4);
-  s->att_ml = (float *)take(m * d.n_heads * S * 2 * 4);
+  s->keyoff = (int64_t *)take(m * (size_t)(d.swa_width > 0 ? d.swa_width : d.window) * 8);
+  (void)S;
   s->ob = (uint16_t *)take(m * HD * 2);
   s->p_t = (float *)take((HD / pl.kc_oa) * m * orr * 4);
   s->tb = (uint16_t *)take(m * orr * 2);

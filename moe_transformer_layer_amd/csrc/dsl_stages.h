@@ -41,7 +41,7 @@ struct Scratch {
   float *p_qkv;            // [nks][M][qr + D]
   uint16_t *qb;            // MXFP8(RMSNorm(q latent)) as bf16 [M][qr]
   float *p_q;              // [nks][M][H*D]
-  float *att_o, *att_ml;   // split partials [M][H][S][D], [M][H][S][2]
+  int64_t *keyoff;         // byte offset in the cache of every key record of each row [M][keys], -1 none
   uint16_t *ob;            // MXFP8(attention output) as bf16 [M][H*D]
   float *p_t;              // [nks][M][or]
   uint16_t *tb;            // MXFP8(wo_a output) as bf16 [M][or]
@@ -252,8 +252,8 @@ __device__ __forceinline__ void step_mfma(const v4u af[NT][4], const float bsc[N
 // NT weight tiles of 16 rows times NCG groups of 16 bf16 activation rows over `nsteps`
 // 128-wide K steps, software-pipelined in groups of 4 steps: ring buffers hold the raw
 // weight bytes and the activation fragments of the next 4 steps and the scales of the
-// next group, so every load is issued a group ahead of its use.  Prefetch addresses
-// are clamped to the last step, so the loop has no branches.  Requires nsteps % 4 == 0
+// next group, so every load is issued a group ahead of its use (the last group loads
+// nothing; the conditions are uniform over the wave).  Requires nsteps % 4 == 0
 // and 16-byte aligned scale rows.  kb = this lane's first activation K index.
 // acc[tt][c] lane l ends holding C[4*(l/16) + r][l%16]: weight row n0[tt] + 4*(l/16) + r,
 // activation row 16c + l%16.
@@ -268,7 +268,7 @@ __device__ __forceinline__ void tiles_pipe4(const WStream ws[NT], int nsteps, co
 #pragma unroll
   for (int tt = 0; tt < NT; tt++) {
     scg[tt] = load_scales4<FMT>(ws[tt], 0);
-    scn[tt] = load_scales4<FMT>(ws[tt], nsteps > P ? P : 0);
+    if (nsteps > P) scn[tt] = load_scales4<FMT>(ws[tt], P);
   }
 #pragma unroll
   for (int j = 0; j < P; j++) {
@@ -281,28 +281,33 @@ __device__ __forceinline__ void tiles_pipe4(const WStream ws[NT], int nsteps, co
     for (int c = 0; c < NCG; c++) load_b(rb[j][c], xrow[c], xok[c], kb + 128 * j);
   }
   for (int s = 0; s < nsteps; s += P) {
+    // the last group issues no loads: a prefetch of a step past the end would only be a
+    // second round trip that the stage waits for
+    const bool more = s + P < nsteps;
 #pragma unroll
     for (int j = 0; j < P; j++) {
       const int st = s + j;
-      const int sn = st + P < nsteps ? st + P : nsteps - 1;
       v4u af[NT][4];
       float bsc[NT];
 #pragma unroll
       for (int tt = 0; tt < NT; tt++) {
         bsc[tt] = scale_of4<FMT>(scg[tt], j, g);
         decode_a<FMT>(ra[j][tt], bsc[tt], af[tt]);
-        load_a<FMT>(ra[j][tt], ws[tt], sn);
+        if (more) load_a<FMT>(ra[j][tt], ws[tt], st + P);
       }
       step_mfma<FMT, NT, NCG>(af, bsc, rb[j % PB], acc);
-      const int snb = st + PB < nsteps ? st + PB : nsteps - 1;
+      if (st + PB < nsteps) {
 #pragma unroll
-      for (int c = 0; c < NCG; c++) load_b(rb[j % PB][c], xrow[c], xok[c], kb + 128 * snb);
+        for (int c = 0; c < NCG; c++) load_b(rb[j % PB][c], xrow[c], xok[c], kb + 128 * (st + PB));
+      }
     }
-    const int gn = s + 2 * P < nsteps ? s + 2 * P : nsteps - P;
+    if (more) {
+      const int gn = s + 2 * P < nsteps ? s + 2 * P : nsteps - P;
 #pragma unroll
-    for (int tt = 0; tt < NT; tt++) {
-      scg[tt] = scn[tt];
-      scn[tt] = load_scales4<FMT>(ws[tt], gn);
+      for (int tt = 0; tt < NT; tt++) {
+        scg[tt] = scn[tt];
+        scn[tt] = load_scales4<FMT>(ws[tt], gn);
+      }
     }
   }
 }
@@ -390,6 +395,26 @@ __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, cons
                            const uint16_t *x, int M, float *part) {
   const int T = (N >> 4) * (K / kc);
   for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+}
+
+// ============================================================== cache prefetch
+
+// Bring 16 bytes into the caches without registers: an LDS-DMA load whose data lands in
+// a scratch LDS area of the wave (lane j writes bytes [16 j, 16 j + 16) of it).
+__device__ __forceinline__ void touch16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Worker `wk` of `nwk` (a wave) fetches its share of [base, base + bytes) into the L2 /
+// Infinity Cache, 1 KB per instruction; 16-byte chunks past the end are skipped.
+__device__ __forceinline__ void prefetch_share(const void *base, size_t bytes, int wk, int nwk, int lane, void *lds) {
+  const size_t per = ((bytes + (size_t)nwk * 1024 - 1) / ((size_t)nwk * 1024)) * 1024;
+  const size_t b0 = (size_t)wk * per, b1 = b0 + per < bytes ? b0 + per : bytes;
+  for (size_t off = b0; off < b1; off += 1024) {
+    const size_t o = off + 16 * (size_t)lane;
+    if (o + 16 <= bytes) touch16((const uint8_t *)base + o, lds);
+  }
 }
 
 // ============================================================== block-level helpers

@@ -54,6 +54,8 @@ def _weights_stub():
     (dict(top_k=9), dsl.DSL_EUNSUPPORTED),
     (dict(inter=100), dsl.DSL_EUNSUPPORTED),
     (dict(n_layers=5), dsl.DSL_EUNSUPPORTED),
+    (dict(window=257), dsl.DSL_EUNSUPPORTED),
+    (dict(swa_width=257), dsl.DSL_EUNSUPPORTED),
     (dict(window=0), dsl.DSL_EINVAL),
     (dict(kv_block=0), dsl.DSL_EINVAL),
 ])
