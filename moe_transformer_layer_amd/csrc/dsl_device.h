@@ -272,50 +272,57 @@ __device__ __forceinline__ void st_f2(float *p, float2 v) { stg(reinterpret_cast
 
 // ------------------------------------------------------------------ grid barrier
 
-// Sync words of a handle (each counter on a 256-byte line of its own).
+// Sync words of a handle (each counter on a 256-byte line of its own).  The counters
+// only grow: after R completed barriers group[g] = (blocks in group g) * R, top =
+// groups * R and every release[g] = R (mod 2^32), so no barrier resets a word.
 struct SyncWords {
-  unsigned group[8][64];  // arrivals per group of blocks (block index mod 8)
-  unsigned top[64];       // groups fully arrived
-  unsigned generation;    // completed barriers (monotonic; the barrier's epoch tag)
-  unsigned pad1[63];
-  unsigned health;        // 0, or a DSL device fault code
+  unsigned group[8][64];    // arrivals per group of blocks (block index mod 8)
+  unsigned top[64];         // groups fully arrived
+  unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
+  unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };
 
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 
+// Barriers completed on this sync state before the launch.  Every block reads it before
+// its first arrival, and no barrier of the launch completes before all blocks have
+// arrived, so every block reads the same value.
+__device__ __forceinline__ unsigned barrier_base(SyncWords *sw) {
+  return __hip_atomic_load(gptr(&sw->release[blockIdx.x & 7u][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // All blocks of the launch meet here.  Each wave first waits for its own memory
 // operations (its write-through stores are then at the device's coherence point), the
 // block meets, and thread 0 arrives with relaxed atomics.  Arrivals are counted in two
 // levels (8 group counters, then one top counter) so no single address takes more than
-// nblocks/8 atomics; the last arrival bumps the generation word the others poll.  No
-// cache maintenance: see stg.  The spin is bounded: a barrier that does not complete
+// nblocks/8 atomics; the last arrival writes the barrier's number into one release word
+// per group, and each group polls its own word, so the polls do not queue behind the
+// counters' atomics.  *next (thread 0's, in LDS) is the number this barrier completes.
+// No cache maintenance: see stg.  The spin is bounded: a barrier that does not complete
 // records kFaultBarrier in the health word and lets the block go on, so the launch
 // always drains.
-__device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks) {
+__device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks, unsigned *next) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned grp = blockIdx.x & 7u;
     const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
     const unsigned per = (nblocks - grp + 7u) / 8u;  // blocks in this group
-    const unsigned gen = __hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned r = *next;
     const unsigned a = __hip_atomic_fetch_add(gptr(&sw->group[grp][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool released = false;
-    if (a == per - 1u) {
-      __hip_atomic_store(gptr(&sw->group[grp][0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a == per * r - 1u) {
       const unsigned b = __hip_atomic_fetch_add(gptr(&sw->top[0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (b == ngroups - 1u) {
-        __hip_atomic_store(gptr(&sw->top[0]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_fetch_add(gptr(&sw->generation), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b == ngroups * r - 1u) {
+        for (unsigned g = 0; g < ngroups; g++)
+          __hip_atomic_store(gptr(&sw->release[g][0]), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         released = true;
       }
     }
     if (!released) {
       unsigned spins = 0;
-      while (__hip_atomic_load(gptr(&sw->generation), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+      while ((int)(__hip_atomic_load(gptr(&sw->release[grp][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - r) < 0) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > (1u << 24)) {
           __hip_atomic_fetch_or(gptr(&sw->health), (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -323,6 +330,7 @@ __device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks) {
         }
       }
     }
+    *next = r + 1u;
   }
   __syncthreads();
 }

@@ -1028,7 +1028,7 @@ struct Tracer {
   do {                        \
     __syncthreads();          \
     tr.mark();                \
-    grid_barrier(sw, nb);     \
+    grid_barrier(sw, nb, &bar_next); \
     tr.mark();                \
   } while (0)
 
@@ -1040,6 +1040,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ Routing R;
   __shared__ float red[16];
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[kWavesPerBlock][4096];  // per-wave scale staging
+  __shared__ unsigned bar_next;  // number of the next grid barrier (thread 0's)
   const unsigned nb = gridDim.x;
   int mode, n_layers;
   SyncWords *sw;
@@ -1051,6 +1052,9 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     sw = kp->sync;
     tr.buf = kp->trace;
   }
+  // the last wave reads the barrier base: it has no work on the first stage's critical
+  // path (the first barrier's __syncthreads publishes the value to thread 0)
+  if (tid() == kThreads - kWave) bar_next = barrier_base(sw) + 1u;
   const bool moe_mode = mode == kModeMoe;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
@@ -1058,16 +1062,6 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     if (!moe_mode) {
       {
         STAGE(l);
-        // blocks this stage leaves idle fetch the next two linears' weights
-        const int busy = 2 * p.M;
-        if (bid() >= busy) {
-          const int nwk = ((int)gridDim.x - busy) * kWavesPerBlock, wk = (bid() - busy) * kWavesPerBlock + cx.wave;
-          void *pf = wave_lds[cx.wave];
-          prefetch_share(w.wqkv, (size_t)(p.qr + p.D) * p.h, wk, nwk, cx.lane, pf);
-          prefetch_share(w.wqkv_s, (size_t)((p.qr + p.D) / 32) * (p.h / 32), wk, nwk, cx.lane, pf);
-          prefetch_share(w.wq_b, (size_t)p.H * p.D * p.qr, wk, nwk, cx.lane, pf);
-          prefetch_share(w.wq_b_s, (size_t)(p.H * p.D / 32) * (p.qr / 32), wk, nwk, cx.lane, pf);
-        }
         const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
           case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
@@ -1095,25 +1089,6 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       SYNC();
       {
         STAGE(l);
-        // blocks the attention leaves idle fetch the weights of wo_a, wo_b, the router and
-        // the shared expert
-        const int per_block = kWavesPerBlock / p.S;
-        const int busy = (p.M * p.H + per_block - 1) / per_block;
-        if (bid() >= busy && mode != kModeMoe) {
-          const int nwk = ((int)gridDim.x - busy) * kWavesPerBlock, wk = (bid() - busy) * kWavesPerBlock + cx.wave;
-          void *pf = wave_lds[cx.wave];
-          prefetch_share(w.wo_a, (size_t)p.orr * p.H * p.D, wk, nwk, cx.lane, pf);
-          prefetch_share(w.wo_a_s, (size_t)(p.orr / 32) * (p.H * p.D / 32), wk, nwk, cx.lane, pf);
-          prefetch_share(w.wo_b, (size_t)p.h * p.orr, wk, nwk, cx.lane, pf);
-          prefetch_share(w.wo_b_s, (size_t)(p.h / 32) * (p.orr / 32), wk, nwk, cx.lane, pf);
-          if (mode == kModeDecode) {
-            prefetch_share(w.w_router, (size_t)p.E * p.h * 4, wk, nwk, cx.lane, pf);
-            prefetch_share(w.sh_w13, (size_t)2 * p.Is * p.h, wk, nwk, cx.lane, pf);
-            prefetch_share(w.sh_w13_s, (size_t)(2 * p.Is / 128) * (p.h / 128) * 4, wk, nwk, cx.lane, pf);
-            prefetch_share(w.sh_wd, (size_t)p.h * p.Is, wk, nwk, cx.lane, pf);
-            prefetch_share(w.sh_wd_s, (size_t)(p.h / 128) * (p.Is / 128) * 4, wk, nwk, cx.lane, pf);
-          }
-        }
         float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
         switch (p.D) {
           case 64: st_attention_v<1>(p, cx, kv, lds); break;

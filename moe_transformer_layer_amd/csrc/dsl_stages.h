@@ -397,26 +397,6 @@ __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, cons
   for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
 }
 
-// ============================================================== cache prefetch
-
-// Bring 16 bytes into the caches without registers: an LDS-DMA load whose data lands in
-// a scratch LDS area of the wave (lane j writes bytes [16 j, 16 j + 16) of it).
-__device__ __forceinline__ void touch16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-// Worker `wk` of `nwk` (a wave) fetches its share of [base, base + bytes) into the L2 /
-// Infinity Cache, 1 KB per instruction; 16-byte chunks past the end are skipped.
-__device__ __forceinline__ void prefetch_share(const void *base, size_t bytes, int wk, int nwk, int lane, void *lds) {
-  const size_t per = ((bytes + (size_t)nwk * 1024 - 1) / ((size_t)nwk * 1024)) * 1024;
-  const size_t b0 = (size_t)wk * per, b1 = b0 + per < bytes ? b0 + per : bytes;
-  for (size_t off = b0; off < b1; off += 1024) {
-    const size_t o = off + 16 * (size_t)lane;
-    if (o + 16 <= bytes) touch16((const uint8_t *)base + o, lds);
-  }
-}
-
 // ============================================================== block-level helpers
 
 // Sum / max over the block's threads (fixed order: wave results in wave order).
