@@ -258,6 +258,12 @@ __device__ __forceinline__ void stg(T *p, T v) {
   }
 }
 __device__ __forceinline__ v4u ld16(const void *p) { return ldg(reinterpret_cast<const v4u *>(p)); }
+// 16 bytes of weights, which a launch reads once: a nontemporal (streaming) load, so the
+// weight stream does not displace cached activations and scratch, and streams faster
+// than cached loads.
+__device__ __forceinline__ v4u ldw16(const void *p) {
+  return __builtin_nontemporal_load(gptr(reinterpret_cast<const v4u *>(p)));
+}
 __device__ __forceinline__ void st16(void *p, v4u v) { stg(reinterpret_cast<v4u *>(p), v); }
 __device__ __forceinline__ float4 ld_f4(const float *p) {
   const v4f t = ldg(reinterpret_cast<const v4f *>(p));

@@ -457,8 +457,9 @@ __device__ __forceinline__ void router_task_j(const Params &p, const float *__re
     const int k = c * kc + 512 * j + 8 * lane;
     on[j] = 512 * j + 8 * lane < kc;
     const float *wp = Wr + (size_t)e * h + (on[j] ? k : c * kc);
-    wv[j][0] = ld_f4(wp);
-    wv[j][1] = ld_f4(wp + 4);
+    const v4u w0 = ldw16(wp), w1 = ldw16(wp + 4);
+    wv[j][0] = make_float4(__uint_as_float(w0[0]), __uint_as_float(w0[1]), __uint_as_float(w0[2]), __uint_as_float(w0[3]));
+    wv[j][1] = make_float4(__uint_as_float(w1[0]), __uint_as_float(w1[1]), __uint_as_float(w1[2]), __uint_as_float(w1[3]));
   }
   for (int m0 = 0; m0 < p.M; m0 += 8) {
     v4u uv[8][J];
@@ -656,28 +657,35 @@ __device__ __forceinline__ void routed_gate_up_task(const Params &p, const dsl_w
   }
 }
 
-template <int NCG>
+// Down projection of one expert on the matrix unit over NT 16-row tiles of output rows
+// (tiles NT tile .. NT tile + NT - 1), for the expert's ce <= 16 NCG pairs.
+template <int NCG, int NT>
 __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weights &w, int e, int p0, int ce, int tile, int lane) {
   const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
   const uint8_t *W = w.ex_wd + (size_t)e * h * (I >> 1);
   const uint8_t *S8 = w.ex_wd_s + (size_t)e * h * (I >> 5);
   const uint16_t *xrow[NCG];
   bool xok[NCG];
-  v4f acc[1][NCG];
+  v4f acc[NT][NCG];
 #pragma unroll
   for (int c = 0; c < NCG; c++) {
     const int j = 16 * c + i;
     xok[c] = j < ce;
     xrow[c] = p.s.zr + (size_t)(p0 + (xok[c] ? j : 0)) * I;
-    acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  const WStream ws[1] = {wstream<kW4>(W, S8, nullptr, I, tile * 16 + i, 0, g)};
-  tiles<kW4, 1, NCG>(ws, I >> 7, xrow, xok, 32 * g, g, acc);
 #pragma unroll
-  for (int c = 0; c < NCG; c++) {
-    const int j = 16 * c + i;
-    if (j < ce) stg(reinterpret_cast<v4f *>(p.s.y + (size_t)(p0 + j) * h + tile * 16 + 4 * g), acc[0][c]);
+    for (int tt = 0; tt < NT; tt++) acc[tt][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  WStream ws[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; tt++) ws[tt] = wstream<kW4>(W, S8, nullptr, I, (tile * NT + tt) * 16 + i, 0, g);
+  tiles<kW4, NT, NCG>(ws, I >> 7, xrow, xok, 32 * g, g, acc);
+#pragma unroll
+  for (int tt = 0; tt < NT; tt++)
+#pragma unroll
+    for (int c = 0; c < NCG; c++) {
+      const int j = 16 * c + i;
+      if (j < ce) stg(reinterpret_cast<v4f *>(p.s.y + (size_t)(p0 + j) * h + (tile * NT + tt) * 16 + 4 * g), acc[tt][c]);
+    }
 }
 
 // ------------------------------------------------------------ routed experts on the VALU
@@ -725,14 +733,18 @@ __device__ __forceinline__ void valu_load_x(const uint16_t *const (&rows)[CE], i
       }
 }
 
-// E8M0 scales of 16 consecutive weight rows (16 x 64 Q bytes) into this wave's LDS
+// E8M0 scales of 16 consecutive weight rows (16 x 64 Q bytes): loaded into registers
+// first, written to this wave's LDS once the task's weight loads are in flight (the
+// write waits for the scale loads only, which were issued before the weights).
 template <int Q>
-__device__ __forceinline__ void valu_stage_scales(const uint8_t *src, uint8_t *dst, int lane) {
+__device__ __forceinline__ void valu_load_scales(const uint8_t *src, int lane, v4u (&t)[Q]) {
 #pragma unroll
-  for (int c = 0; c < Q; c++) {
-    const v4u t = ld16(src + 16 * (lane + 64 * c));
-    *reinterpret_cast<v4u *>(dst + 16 * (lane + 64 * c)) = t;
-  }
+  for (int c = 0; c < Q; c++) t[c] = ld16(src + 16 * (lane + 64 * c));
+}
+template <int Q>
+__device__ __forceinline__ void valu_store_scales(uint8_t *dst, int lane, const v4u (&t)[Q]) {
+#pragma unroll
+  for (int c = 0; c < Q; c++) *reinterpret_cast<v4u *>(dst + 16 * (lane + 64 * c)) = t[c];
 }
 
 constexpr int kValuDepth = 16;  // weight rows in flight per wave
@@ -759,18 +771,23 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
   for (int m = 0; m < CE; m++) rows[m] = u + (size_t)R.pair_row[p0 + (m < ce ? m : 0)] * h;
   uint32_t xv[Q][CE][16];
   valu_load_x<CE, Q>(rows, lane, xv);
-  valu_stage_scales<Q>(S + (size_t)(tile * 16) * NB, sl, lane);
-  valu_stage_scales<Q>(S + (size_t)(I + tile * 16) * NB, sl + 16 * NB, lane);
+  v4u scg[Q], scu[Q];
+  valu_load_scales<Q>(S + (size_t)(tile * 16) * NB, lane, scg);
+  valu_load_scales<Q>(S + (size_t)(I + tile * 16) * NB, lane, scu);
   // weight row r of the task in processing order: group r / G, gate rows then up rows
   auto row_of = [&](int r) -> int {
     const int gi = r / G, rr = r % G;
     return (rr >= H ? I : 0) + tile * 16 + gi * H + rr % H;
   };
   v4u ring[DEPTH][Q];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < DEPTH; r++)
 #pragma unroll
-    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)row_of(r) * row_bytes + 16 * (lane + 64 * q));
+    for (int q = 0; q < Q; q++) ring[r][q] = ldw16(W + (size_t)row_of(r) * row_bytes + 16 * (lane + 64 * q));
+  __builtin_amdgcn_sched_barrier(0);
+  valu_store_scales<Q>(sl, lane, scg);
+  valu_store_scales<Q>(sl + 16 * NB, lane, scu);
   float acc[16];
 #pragma unroll
   for (int r = 0; r < NR; r++) {
@@ -785,7 +802,7 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
     if (r + DEPTH < NR) {
 #pragma unroll
       for (int q = 0; q < Q; q++)
-        ring[r % DEPTH][q] = ld16(W + (size_t)row_of(r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
+        ring[r % DEPTH][q] = ldw16(W + (size_t)row_of(r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
     }
 #pragma unroll
     for (int q = 0; q < Q; q++) {
@@ -821,14 +838,19 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   for (int m = 0; m < CE; m++) rows[m] = p.s.zr + (size_t)(p0 + (m < ce ? m : 0)) * I;
   uint32_t xv[Q][CE][16];
   valu_load_x<CE, Q>(rows, lane, xv);
+  v4u sc[NR / 16][Q];
 #pragma unroll
-  for (int b = 0; b < NR / 16; b++) valu_stage_scales<Q>(S + (size_t)(tile * NR + 16 * b) * NB, sl + 16 * NB * b, lane);
+  for (int b = 0; b < NR / 16; b++) valu_load_scales<Q>(S + (size_t)(tile * NR + 16 * b) * NB, lane, sc[b]);
   constexpr int DEPTH = kValuDepth / Q;
   v4u ring[DEPTH][Q];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < DEPTH; r++)
 #pragma unroll
-    for (int q = 0; q < Q; q++) ring[r][q] = ld16(W + (size_t)(tile * NR + r) * row_bytes + 16 * (lane + 64 * q));
+    for (int q = 0; q < Q; q++) ring[r][q] = ldw16(W + (size_t)(tile * NR + r) * row_bytes + 16 * (lane + 64 * q));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < NR / 16; b++) valu_store_scales<Q>(sl + 16 * NB * b, lane, sc[b]);
   float acc[16];
 #pragma unroll
   for (int r = 0; r < NR; r++) {
@@ -843,7 +865,7 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
     if (r + DEPTH < NR) {
 #pragma unroll
       for (int q = 0; q < Q; q++)
-        ring[r % DEPTH][q] = ld16(W + (size_t)(tile * NR + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
+        ring[r % DEPTH][q] = ldw16(W + (size_t)(tile * NR + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
     }
 #pragma unroll
     for (int q = 0; q < Q; q++) {
@@ -885,14 +907,10 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
   }
 }
 
-// Shared down partials, then routed down tasks (expert, 16-row tile), task t to wave t mod waves
-__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
-                                        uint8_t *sl) {
-  const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
-  for (int t = cx.gw; t < TS; t += cx.nw)
-    linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
-  // tiles of TR output rows (TR / 16 tasks on the matrix-core path)
-  constexpr int TR = 16;
+// Routed down tasks (expert, tile of TR output rows), task t to wave t mod waves
+template <int TR>
+__device__ __forceinline__ void st_routed_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
+                                               uint8_t *sl) {
   const int tiles_n = p.h / TR;
   const int T = R.nd * tiles_n;
   const int qv = p.I == 2048 ? 1 : p.I == 4096 ? 2 : 0;  // VALU path: K = 2048 q
@@ -909,18 +927,28 @@ __device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const ds
     } else if (qv == 2 && ce <= 2) {
       if (ce == 1) routed_down_valu<1, 2, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
       else routed_down_valu<2, 2, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
+    } else if (ncg == 1) {
+      routed_down_task<1, TR / 16>(p, w, e, p0, ce, tile, cx.lane);
+    } else if (ncg == 2) {
+      routed_down_task<2, TR / 16>(p, w, e, p0, ce, tile, cx.lane);
     } else {
-      for (int sub = 0; sub < TR / 16; sub++) {
-        const int t16 = tile * (TR / 16) + sub;
-        if (ncg == 1)
-          routed_down_task<1>(p, w, e, p0, ce, t16, cx.lane);
-        else if (ncg == 2)
-          routed_down_task<2>(p, w, e, p0, ce, t16, cx.lane);
-        else
-          routed_down_task<3>(p, w, e, p0, ce, t16, cx.lane);
-      }
+      routed_down_task<3, TR / 16>(p, w, e, p0, ce, tile, cx.lane);
     }
   }
+}
+
+// Shared down partials, then the routed down tasks: tiles of 16 output rows for a few
+// rows (more tasks to spread over the waves), 32 when the step is wide (each task's
+// activation rows are then read once per 32 weight rows).
+__device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
+                                        uint8_t *sl) {
+  const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
+  for (int t = cx.gw; t < TS; t += cx.nw)
+    linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
+  if (p.M > 8)
+    st_routed_down<32>(p, cx, w, R, sl);
+  else
+    st_routed_down<16>(p, cx, w, R, sl);
 }
 
 // m = shared + sum_j w_j y_j in float32 (shared first, slots in emission order);

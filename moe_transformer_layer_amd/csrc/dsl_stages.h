@@ -165,10 +165,12 @@ __device__ __forceinline__ WStream wstream(const uint8_t *W, const uint8_t *S8, 
 template <int FMT>
 __device__ __forceinline__ void load_a(RawA &r, const WStream &ws, int step) {
   if constexpr (FMT == kW4) {
+    // a lane's 16 bytes are half of a 128-byte line whose other half the next step
+    // reads: a cached load, so the line is fetched once
     r.a0 = ld16(ws.w + 64 * step);
   } else {
-    r.a0 = ld16(ws.w + 128 * step);
-    r.a1 = ld16(ws.w + 128 * step + 16);
+    r.a0 = ldw16(ws.w + 128 * step);
+    r.a1 = ldw16(ws.w + 128 * step + 16);
   }
 }
 
