@@ -252,9 +252,9 @@ __device__ __forceinline__ uint64_t load_codes(const uint8_t *p) {
 // with k = v = scale * e4m3(codes) of the record; returns the partial max, the sum of
 // exponentials and (lane l: dims [V l, V l + V)) the exponential-weighted sum of values.
 // Lane j < 32 reads key j's record offset and scale; each key's offset reaches the wave
-// as a scalar (readlane), every lane loads its V dims of the 32 keys at once and keeps
-// them for the value pass, and the 32 dot products are summed across the wave by the
-// transposing butterfly, 16 keys at a time.
+// as a scalar (readlane), every lane loads its V dims of all 32 keys in one batch and
+// keeps them in registers for the value pass, and the 32 dot products are summed across
+// the wave by the transposing butterfly, 16 keys at a time.
 template <int V>
 __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane,
                                           float &mx_out, float &l_out, float (&o)[V]) {
@@ -274,20 +274,21 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   auto key_off = [&](int j) -> int64_t {
     return (int64_t)(((uint64_t)__builtin_amdgcn_readlane(ohi, j) << 32) | __builtin_amdgcn_readlane(olo, j));
   };
+  // every lane's V dims of the 32 keys, loaded in one batch and kept for the value pass
+  uint64_t codes[kSplitKeys];
+#pragma unroll
+  for (int j = 0; j < kSplitKeys; j++) {
+    const int64_t off = key_off(j);
+    codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
+  }
   float sc[2];
 #pragma unroll
   for (int hf = 0; hf < 2; hf++) {
-    uint64_t codes[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int64_t off = key_off(16 * hf + j);
-      codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
-    }
     float d[16];
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       float c[V];
-      decode_codes<V>(codes[j], c);
+      decode_codes<V>(codes[16 * hf + j], c);
       float a = 0.f;
 #pragma unroll
       for (int v = 0; v < V; v++) a += q[v] * c[v];
@@ -302,25 +303,19 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   const float pj = my == -INFINITY ? 0.f : expf(my - mx);
   const float l = wave_sum(pj);
   const float f = pj * mysc;
-  // values: the same records again (cache hits), weighted by exp(score - max) * scale
+  // values: the same codes, weighted by exp(score - max) * scale (the empty asm makes
+  // the compiler decode them again here instead of keeping all decoded values live)
+#pragma unroll
+  for (int j = 0; j < kSplitKeys; j++) asm volatile("" : "+v"(codes[j]));
 #pragma unroll
   for (int v = 0; v < V; v++) o[v] = 0.f;
 #pragma unroll
-  for (int hf = 0; hf < 2; hf++) {
-    uint64_t codes[16];
+  for (int j = 0; j < kSplitKeys; j++) {
+    const float fj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), j));
+    float c[V];
+    decode_codes<V>(codes[j], c);
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int64_t off = key_off(16 * hf + j);
-      codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float fj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), 16 * hf + j));
-      float c[V];
-      decode_codes<V>(codes[j], c);
-#pragma unroll
-      for (int v = 0; v < V; v++) o[v] += fj * c[v];
-    }
+    for (int v = 0; v < V; v++) o[v] += fj * c[v];
   }
   mx_out = mx;
   l_out = l;
@@ -332,8 +327,11 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
 // 32-block spans 32 / V lanes) and stores it.  Pad rows give zeros.
 template <int V>
 __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds) {
-  const int S = p.S, P = kWavesPerBlock / S, D = p.D;
+  const int S = p.S, D = p.D;
   const int T = p.M * p.H;
+  // items per block: one when the grid has a block per item (the item's split waves then
+  // have a SIMD each), else as many as the block's waves hold
+  const int P = T <= (int)gridDim.x ? 1 : kWavesPerBlock / S;
   const int w = cx.wave, lane = cx.lane, i = w / S, sp = w - i * S;
   float *lo_ = lds, *lml = lds + kWavesPerBlock * D;
   for (int t0 = bid() * P; t0 < T; t0 += gridDim.x * P) {
@@ -343,7 +341,8 @@ __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, c
       float mx = -INFINITY, l = 0.f, o[V];
 #pragma unroll
       for (int v = 0; v < V; v++) o[v] = 0.f;
-      if (ldg(p.pos + m) >= 0) attn_item<V>(p, kv, m, hh, sp, lane, mx, l, o);
+      // a pad row's key offsets are all -1, so its item gives zeros
+      attn_item<V>(p, kv, m, hh, sp, lane, mx, l, o);
 #pragma unroll
       for (int v = 0; v < V; v++) lo_[w * D + lane * V + v] = o[v];
       if (lane == 0) {
