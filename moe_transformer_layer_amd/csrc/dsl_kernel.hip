@@ -514,23 +514,21 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
   }
 }
 
-// Top-k of row m (one wave): the router's partial logits summed in chunk order, k rounds
-// of wave arg-max on (logit, lower id first) keys, so ties go to the lower id and the
-// selected ids come out in descending logit order; weights = softmax of the selected
-// logits.  Pad rows select nothing (ids -1, weights 0).
-__device__ __forceinline__ void topk_row(const Params &p, int m, bool live, int lane, float *logits_tap) {
-  const int k = p.k, E = p.E, M = p.M, nc = p.h / p.pl.kc_router;
-  const float *lg = p.s.logits + (size_t)m * E;
-  const size_t cs = (size_t)M * E;
-  const int l0 = lane < E ? lane : 0, l1 = lane + 64 < E ? lane + 64 : 0;
-  float a0 = sum_strided(lg + l0, cs, nc), a1 = sum_strided(lg + l1, cs, nc);
-  if (logits_tap) {
-    if (lane < E) stg(logits_tap + (size_t)m * E + lane, a0);
-    if (lane + 64 < E) stg(logits_tap + (size_t)m * E + lane + 64, a1);
-  }
-  if (lane >= E) a0 = -INFINITY;
-  if (lane + 64 >= E) a1 = -INFINITY;
-  uint64_t k0 = amax_key(a0, lane), k1 = amax_key(a1, lane + 64);
+// Top-k of one row's router logits (one wave; two experts per lane, v0 for expert lane
+// and v1 for expert lane + 64): k rounds of a branch-free wave arg-max on (logit, lower
+// id first) keys, so ties go to the lower id and the selections come out in descending
+// logit order; the weights are a softmax over the selected k.  Lane j < k returns the
+// j-th selection (id -1 and weight 0 for a pad row).
+struct TopkLane {
+  int id;
+  float w;
+};
+
+__device__ __forceinline__ TopkLane topk_select(const Params &p, int lane, float v0, float v1, bool live) {
+  const int k = p.k, E = p.E;
+  if (lane >= E) v0 = -INFINITY;
+  if (lane + 64 >= E) v1 = -INFINITY;
+  uint64_t k0 = amax_key(v0, lane), k1 = amax_key(v1, lane + 64);
   int myid = -1;
   float myval = -INFINITY;
   for (int j = 0; j < k; j++) {
@@ -548,23 +546,72 @@ __device__ __forceinline__ void topk_row(const Params &p, int m, bool live, int 
   sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0xB1, 0xF, 0xF, false));   // quad xor 1
   sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x4E, 0xF, 0xF, false));   // quad xor 2
   sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x141, 0xF, 0xF, false));  // half-row mirror
-  if (lane < k) {
-    stg(p.s.tk_ids + (size_t)m * k + lane, live ? (int32_t)myid : (int32_t)-1);
-    stg(p.s.tk_w + (size_t)m * k + lane, live ? ev / sum : 0.f);
+  return TopkLane{live ? myid : -1, live ? ev / sum : 0.f};
+}
+
+// The logits of row m (the router's split-K partials summed in chunk order) for experts
+// lane and lane + 64; the logits tap, when given, receives them.
+__device__ __forceinline__ void row_logits(const Params &p, int m, int lane, float &v0, float &v1, float *logits_tap) {
+  const int E = p.E, nc = p.h / p.pl.kc_router;
+  const size_t cs = (size_t)p.M * E;
+  const float *lg = p.s.logits + (size_t)m * E;
+  v0 = sum_strided(lg + (lane < E ? lane : 0), cs, nc);
+  v1 = sum_strided(lg + (lane + 64 < E ? lane + 64 : 0), cs, nc);
+  if (logits_tap) {
+    if (lane < E) stg(logits_tap + (size_t)m * E + lane, v0);
+    if (lane + 64 < E) stg(logits_tap + (size_t)m * E + lane + 64, v1);
   }
 }
 
-// Routing of the current layer in every block's LDS, from the selected ids and weights:
+// Steps of at most one row per wave of a block select in every block: wave m takes row
+// m (the same arithmetic in every block, so the same ids everywhere), into R.ids / R.w
+// ([M][k]).  No grid barrier is then needed between the router and the experts.
+constexpr int kTopkInBlockRows = kWavesPerBlock;
+
+__device__ __forceinline__ void topk_in_block(const Params &p, const Ctx &cx, Routing &R, bool all_live,
+                                              float *logits_tap) {
+  const int m = cx.wave;
+  if (m >= p.M) return;
+  float v0, v1;
+  row_logits(p, m, cx.lane, v0, v1, logits_tap);
+  const TopkLane t = topk_select(p, cx.lane, v0, v1, all_live || ldg(p.pos + m) >= 0);
+  if (cx.lane < p.k) {
+    R.ids[m * p.k + cx.lane] = t.id;
+    R.w[m * p.k + cx.lane] = t.w;
+  }
+}
+
+// Wider steps: one wave per row over the grid, into the scratch ids / weights; every
+// block copies them into its R after the next grid barrier.
+__device__ __forceinline__ void topk_in_grid(const Params &p, const Ctx &cx, bool all_live, float *logits_tap) {
+  const int m = cx.gw;
+  if (m >= p.M) return;
+  float v0, v1;
+  row_logits(p, m, cx.lane, v0, v1, logits_tap);
+  const TopkLane t = topk_select(p, cx.lane, v0, v1, all_live || ldg(p.pos + m) >= 0);
+  if (cx.lane < p.k) {
+    stg(p.s.tk_ids + (size_t)m * p.k + cx.lane, (int32_t)t.id);
+    stg(p.s.tk_w + (size_t)m * p.k + cx.lane, t.w);
+  }
+}
+
+__device__ __forceinline__ void topk_from_grid(const Params &p, Routing &R) {
+  for (int t = tid(); t < p.M * p.k; t += kThreads) {
+    R.ids[t] = ldg(p.s.tk_ids + t);
+    R.w[t] = ldg(p.s.tk_w + t);
+  }
+}
+
+// Routing of the current layer in every block's LDS, from the selected ids and weights
+// (R.ids / R.w):
 // per expert the set of rows that chose it, the distinct-expert list in id order and
 // the (row, slot) -> pair map ordered by expert, then by row.
 __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R) {
   const int k = p.k, M = p.M, t0 = tid();
   for (int e = t0; e < 128; e += kThreads) R.rows[e] = 0ull;
-  __syncthreads();
+  __syncthreads();  // also publishes R.ids / R.w
   for (int t = t0; t < M * k; t += kThreads) {
-    const int id = ldg(p.s.tk_ids + t);
-    R.ids[t] = id;
-    R.w[t] = ldg(p.s.tk_w + t);
+    const int id = R.ids[t];
     if (id >= 0) atomicOr(&R.rows[id], 1ull << (t / k));
   }
   __syncthreads();
@@ -1170,14 +1217,17 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     SYNC();
     {
       STAGE(l);
-      // one wave per row selects its experts; every block takes part in the shared SwiGLU
-      if (cx.gw < p.M)
-        topk_row(p, cx.gw, moe_mode || ldg(p.pos + cx.gw) >= 0, cx.lane, last ? p.taps.logits : nullptr);
-      st_shared_swiglu(p, moe_mode);
-    }
-    SYNC();
-    {
-      STAGE(l);
+      if (p.M <= kTopkInBlockRows) {
+        // no grid barrier between the router and the experts: every block selects the
+        // experts of every row itself
+        topk_in_block(p, cx, R, moe_mode, last && bid() == 0 ? p.taps.logits : nullptr);
+        tr.mark();
+        tr.mark();
+      } else {
+        topk_in_grid(p, cx, moe_mode, last ? p.taps.logits : nullptr);
+        SYNC();
+        topk_from_grid(p, R);
+      }
       build_routing(p, cx, R);
       if (bid() == 0 && p.taps.layer_ids)
         for (int t = tid(); t < p.M * p.k; t += kThreads)
@@ -1193,6 +1243,9 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     {
       STAGE(l);
       st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
+      // the shared SwiGLU, off the critical path: its reader, the shared down projection,
+      // comes after the next grid barrier
+      st_shared_swiglu(p, moe_mode);
     }
     SYNC();
     {

@@ -50,7 +50,7 @@ struct Scratch {
   uint16_t *hres;          // bf16 residual after attention [M][h]
   uint16_t *u;             // bf16 MoE input [M][h]
   float *logits;           // router partial logits [hidden / kc_router][M][E]
-  int32_t *tk_ids;         // selected experts [M][k] (descending logit; -1 for pad rows)
+  int32_t *tk_ids;         // selected experts of steps wider than a block's waves [M][k]
   float *tk_w;             // their weights [M][k]
   float *p_sh;             // [nks][M][2*Is]
   uint16_t *zsh;           // bf16 shared SwiGLU output [M][Is]
