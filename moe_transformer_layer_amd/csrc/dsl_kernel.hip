@@ -52,17 +52,16 @@ __device__ __forceinline__ void key_offsets_row(const Params &p, const dsl_kv &k
   }
 }
 
-// RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values); the
-// block of row m also resolves the row's key records.
+// RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values).
 template <int E>
 __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const dsl_kv &kv,
                                                const uint16_t *xin, float *red) {
   const int n = p.h, k = tid() * E;
   const bool act = k < n;
-  // the key records of row m are resolved by block M + m (or by block m itself when the
-  // grid has fewer than 2 M blocks), in parallel with the norm
-  const bool split = (int)gridDim.x >= 2 * p.M;
-  if (split && bid() >= p.M && bid() < 2 * p.M) key_offsets_row(p, kv, bid() - p.M);
+  // with fewer than 3 M blocks the key records of row m are resolved here, by block M + m
+  // (or by block m itself with fewer than 2 M blocks); else by the qkv_post stage
+  const bool late = (int)gridDim.x >= 3 * p.M, split = (int)gridDim.x >= 2 * p.M;
+  if (!late && split && bid() >= p.M && bid() < 2 * p.M) key_offsets_row(p, kv, bid() - p.M);
   for (int m = bid(); m < p.M; m += gridDim.x) {
     if (!split) key_offsets_row(p, kv, m);
     float v[E];
@@ -185,10 +184,12 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
                                             uint8_t *tmp) {
   const int eq = row_elems(p.qr), ekv = row_elems(p.D);
-  // q of row m on block m, kv of row m on block M + m (both on block m when the grid has
-  // fewer than 2 M blocks)
+  // q of row m on block m, kv of row m on block M + m, row m's key offsets on block 2 M + m
+  // (with fewer than 3 M blocks the key offsets come from the norm stage, with fewer than
+  // 2 M all of a row's work is block m's)
   if ((int)gridDim.x >= 2 * p.M) {
     const int b = bid();
+    if (b >= 2 * p.M && b < 3 * p.M) key_offsets_row(p, kv, b - 2 * p.M);
     if (b < p.M) {
       switch (eq) {
         case 1: qpost_row<1>(p, w, b, red); break;
