@@ -64,33 +64,23 @@ __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weight
   if (!late && split && bid() >= p.M && bid() < 2 * p.M) key_offsets_row(p, kv, bid() - p.M);
   for (int m = bid(); m < p.M; m += gridDim.x) {
     if (!split) key_offsets_row(p, kv, m);
-    float v[E];
+    float v[E], gm[E];
     if (act)
       load_bf16<E>(xin + (size_t)m * n + k, v);
     else
 #pragma unroll
       for (int e = 0; e < E; e++) v[e] = 0.f;
+    load_f32<E>(w.attn_norm + k, act, gm);  // with the row, not after the reduction's barrier
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; e++) ss += v[e] * v[e];
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
 #pragma unroll
-    for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * ldg(w.attn_norm + k + e) : 0.f;
+    for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * gm[e] : 0.f;
     mx_quant_dequant<E>(v);
     if (act) store_bf16<E>(p.s.xb + (size_t)m * n + k, v);
   }
-}
-
-// Physical record of a slot, or null (with a recorded fault) if the slot is outside
-// the cache view.
-__device__ __forceinline__ uint8_t *record_ptr(const Params &p, const dsl_kv &kv, int64_t slot) {
-  const int64_t blk = slot / p.B;
-  if (slot < 0 || blk >= kv.n_blocks) {
-    __hip_atomic_fetch_or(gptr(&p.sync->health), (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return nullptr;
-  }
-  return kv.base + blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
 }
 
 // Byte offset of a slot's record in the cache, or -1 (with a recorded fault) if the slot
@@ -117,19 +107,20 @@ template <int E>
 __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red) {
   const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.qr, k = tid() * E;
   const bool act = k < n;
-  float v[E];
+  float v[E], gm[E];
   if (act)
     load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + k, (size_t)p.M * N, nks, v);
   else
 #pragma unroll
     for (int e = 0; e < E; e++) v[e] = 0.f;
+  load_f32<E>(w.q_norm + k, act, gm);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; e++) ss += v[e] * v[e];
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
 #pragma unroll
-  for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * ldg(w.q_norm + k + e) : 0.f;
+  for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * gm[e] : 0.f;
   mx_quant_dequant<E>(v);
   if (act) store_bf16<E>(p.s.qb + (size_t)m * n + k, v);
 }
@@ -141,12 +132,16 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
                                            uint8_t *tmp) {
   const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = tid() * E;
   const bool act = k < n;
-  float v[E];
+  float v[E], gm[E];
   if (act)
     load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + p.qr + k, (size_t)p.M * N, nks, v);
   else
 #pragma unroll
     for (int e = 0; e < E; e++) v[e] = 0.f;
+  load_f32<E>(w.kv_norm + k, act, gm);
+  // the record's place, resolved (position, request, block table) while the row reduces
+  const int pos = ldg(p.pos + m);
+  const int64_t slot = pos >= 0 ? slot_of(p, kv, ldg(kv.row_req + m), pos) : (int64_t)-1;
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; e++) ss += v[e] * v[e];
@@ -155,20 +150,19 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
   float am = 0.f;
 #pragma unroll
   for (int e = 0; e < E; e++) {
-    v[e] = act ? v[e] * r * ldg(w.kv_norm + k + e) : 0.f;
+    v[e] = act ? v[e] * r * gm[e] : 0.f;
     am = fmaxf(am, fabsf(v[e]));
   }
   am = block_max(am, red);
-  const int pos = ldg(p.pos + m);
   if (pos < 0) return;  // pad row: no KV write
   const float sc = am / 448.0f;
-  uint8_t *rec = nullptr;
-  if (tid() == 0) rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
-  __syncthreads();
-  if (tid() == 0) red[8] = __uint_as_float((uint32_t)(rec ? 1u : 0u));
-  __syncthreads();
-  if (red[8] == 0.f) return;
-  rec = record_ptr(p, kv, slot_of(p, kv, ldg(kv.row_req + m), pos));
+  const int64_t blk = slot / p.B;
+  if (slot < 0 || blk >= kv.n_blocks) {  // outside the cache view: recorded, no write
+    if (tid() == 0)
+      __hip_atomic_fetch_or(gptr(&p.sync->health), (unsigned)kFaultSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  uint8_t *rec = kv.base + blk * kv.block_stride + (slot - blk * p.B) * (int64_t)(p.D + 16);
   // codes gathered in LDS, then written as 16-byte stores
   if (act) {
 #pragma unroll
@@ -404,7 +398,7 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
   const bool act = k < h;
   for (int m = bid(); m < p.M; m += gridDim.x) {
     const bool live = ldg(p.pos + m) >= 0;
-    float a[E], hr[E];
+    float a[E], hr[E], gm[E];
     if (act) {
       load_sum_f32<E>(p.s.p_a + (size_t)m * h + k, (size_t)p.M * h, nks, a);
       load_bf16<E>(xin + (size_t)m * h + k, hr);
@@ -412,6 +406,7 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
 #pragma unroll
       for (int e = 0; e < E; e++) a[e] = hr[e] = 0.f;
     }
+    load_f32<E>(w.ffn_norm + k, act && p.mode != kModeAttn, gm);
 #pragma unroll
     for (int e = 0; e < E; e++) {
       a[e] = live ? a[e] : 0.f;
@@ -433,7 +428,7 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
     if (last && p.taps.attn_out) store_bf16<E>((uint16_t *)p.taps.attn_out + off, a);
     float uu[E];
 #pragma unroll
-    for (int e = 0; e < E; e++) uu[e] = live ? hr[e] * r * ldg(w.ffn_norm + k + e) : 0.f;
+    for (int e = 0; e < E; e++) uu[e] = live ? hr[e] * r * gm[e] : 0.f;
     store_bf16<E>(p.s.u + off, uu);
     if (last && p.taps.moe_in) store_bf16<E>((uint16_t *)p.taps.moe_in + off, uu);
   }

@@ -481,6 +481,22 @@ __device__ __forceinline__ void load_bf16(const uint16_t *p, float v[E]) {
   }
 }
 
+// E consecutive floats (16-byte loads when E >= 4; p then 16-byte aligned), or zeros
+template <int E>
+__device__ __forceinline__ void load_f32(const float *p, bool on, float v[E]) {
+  if constexpr (E >= 4) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const v4u a = on ? ld16(p + e) : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < 4; q++) v[e + q] = __uint_as_float(a[q]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e++) v[e] = on ? ldg(p + e) : 0.f;
+  }
+}
+
 template <int E>
 __device__ __forceinline__ void store_bf16(uint16_t *p, const float v[E]) {
   if constexpr (E >= 8) {
