@@ -62,7 +62,9 @@ def test_tiny_layer_m1(dsl):
     run_decode(dsl, case, res, caches, W_TOL_LAYER)
 
 
-@pytest.mark.parametrize("n_req,rows,n_pad", [(2, 6, 1), (1, 5, 0), (3, 4, 0)])
+# M = 8 and 9 sit on either side of the width up to which every block selects the experts
+# itself (no grid barrier before the routing)
+@pytest.mark.parametrize("n_req,rows,n_pad", [(2, 6, 1), (1, 5, 0), (3, 4, 0), (2, 4, 0), (1, 8, 1)])
 def test_mid_layer_ragged(dsl, n_req, rows, n_pad):
     case, (res, caches) = _decode_case("mid", f"mid_{n_req}x{rows}+{n_pad}", first=100,
                                        n_req=n_req, rows_per_req=rows, n_pad=n_pad)
