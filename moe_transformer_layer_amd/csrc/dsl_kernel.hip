@@ -316,10 +316,11 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   l_out = l;
 }
 
-// Attention and the log-sum-exp combine in one stage: a block takes P = 8 / S (row, head)
-// items at a time, one wave per split; the splits' partials meet in LDS (lds: 8 D + 16
-// floats), where one wave per item combines them, quantizes the output to MXFP8 (a
-// 32-block spans 32 / V lanes) and stores it.  Pad rows give zeros.
+// Attention and the log-sum-exp combine in one stage: a block takes P (row, head) items
+// at a time (one if the grid has a block per item, else 8 / S), one wave per split; the
+// splits' partials meet in LDS (lds: 8 D + 16 floats), where one wave per item combines
+// them, quantizes the output to MXFP8 (a 32-block spans 32 / V lanes) and stores it.
+// Pad rows give zeros.
 template <int V>
 __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds) {
   const int S = p.S, D = p.D;

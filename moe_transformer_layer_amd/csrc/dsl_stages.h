@@ -1,11 +1,12 @@
-// Building blocks of the decode-layer stages: row normalization / MX quantization,
-// weight-streaming linears on the bf16 matrix unit, and the device task queue.
+// Building blocks of the decode-layer stages: launch parameters and scratch, the
+// weight-streaming linears on the bf16 matrix unit, and row helpers (reductions, MX
+// quantization, bf16 loads and stores).
 //
 // Stage list: "Mono decode layer for DeepSeek-V4.1-Flash on MI355X" (vLLM PR
 // 60397), Purpose, launch table (K1: seam, wqkv, q/kv norms, KV insert, wq_b;
 // K2: split attention, combine, wo_a, wo_b, MoE router, top-k, shared expert,
 // MXFP4 experts).  Every stage is called by all blocks of the persistent launch
-// and splits its work over waves; grid barriers separate stages.
+// and splits its work statically over waves; grid barriers separate the stages.
 //
 // Linears.  Every weight format the layer stores decodes exactly into bf16 once
 // its power-of-two block scale is folded in (e4m3 has 4 significant bits, e2m1
