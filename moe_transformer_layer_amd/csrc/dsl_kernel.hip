@@ -601,7 +601,7 @@ __device__ __forceinline__ void topk_from_grid(const Params &p, Routing &R) {
 
 // Routing of the current layer in every block's LDS, from the selected ids and weights
 // (R.ids / R.w):
-// per expert the set of rows that chose it, the distinct-expert list in id order and
+// per expert the set of rows that chose it, the distinct-expert list and
 // the (row, slot) -> pair map ordered by expert, then by row.
 __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Routing &R) {
   const int k = p.k, M = p.M, t0 = tid();
@@ -612,7 +612,7 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     if (id >= 0) atomicOr(&R.rows[id], 1ull << (t / k));
   }
   __syncthreads();
-  // counts, starts (exclusive scan in expert order) and the compacted expert list:
+  // counts, starts (exclusive scan in expert order) and the distinct-expert list:
   // wave 0, experts lane and lane + 64
   if (cx.wave == 0) {
     const int lane = cx.lane;
@@ -630,12 +630,30 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     const int tot0 = __shfl(s0, kWave - 1, kWave);
     R.start[lane] = s0 - c0;
     R.start[lane + 64] = tot0 + s1 - c1;
-    const unsigned long long b0 = __ballot(c0 > 0), b1 = __ballot(c1 > 0);
+    // the distinct experts: in id order for a step of at most 8 rows; wider steps take
+    // the experts with more rows first (then by id), so that the round-robin task order
+    // gives every wave an even share of the matrix-core experts
     const unsigned long long below = (1ull << lane) - 1ull;
-    const int n0 = __popcll(b0);
-    if (c0 > 0) R.list[__popcll(b0 & below)] = lane;
-    if (c1 > 0) R.list[n0 + __popcll(b1 & below)] = lane + 64;
-    if (lane == 0) R.nd = n0 + __popcll(b1);
+    int cmax = 0;
+    if (M > 8) {
+      cmax = c0 > c1 ? c0 : c1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int t = __shfl_xor(cmax, o, kWave);
+        cmax = t > cmax ? t : cmax;
+      }
+    }
+    int at = 0;
+    for (int c = cmax; c >= 0; c--) {
+      // c = 0 takes every expert with rows (all of them in id order when M <= 8)
+      const bool in0 = c > 0 ? c0 == c : (M <= 8 && c0 > 0), in1 = c > 0 ? c1 == c : (M <= 8 && c1 > 0);
+      const unsigned long long b0 = __ballot(in0), b1 = __ballot(in1);
+      const int n0 = __popcll(b0);
+      if (in0) R.list[at + __popcll(b0 & below)] = lane;
+      if (in1) R.list[at + n0 + __popcll(b1 & below)] = lane + 64;
+      at += n0 + __popcll(b1);
+    }
+    if (lane == 0) R.nd = at;
   }
   __syncthreads();
   // pair of (row m, slot): the expert's start plus the rows before m that chose it
