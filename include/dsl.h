@@ -34,7 +34,8 @@
  *     this kernel), and its stages meet at grid barriers, so it needs every block
  *     resident at once: give it the device.  A concurrent kernel that holds compute
  *     units only delays it; one that holds them past the barrier's bounded wait
- *     (about half a second) makes the step report DSL_EDEVICE instead of hanging.
+ *     (2^24 polls of the release word, each a device-memory round trip) makes the
+ *     step report DSL_EDEVICE instead of hanging.
  *   - positions[r] = -1 marks a pad row: no KV write, ids -1, weights 0 and zero
  *     rows in every output ("Test Plan": the kernels skip pad rows, whose slot
  *     is -1).  Rows of one request must have distinct positions.
