@@ -146,15 +146,24 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank-line or indentation differences."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources and the header the library is built from: a stored
-    traffic measurement is used only for the kernel it was taken on."""
+    """Hash of the code (comments left out) of the HIP sources and the header the library
+    is built from: a stored traffic measurement is used only for the kernel it was taken
+    on."""
     import hashlib
     hsh = hashlib.sha256()
     for rel in ("moe_transformer_layer_amd/csrc/dsl_kernel.hip", "moe_transformer_layer_amd/csrc/dsl_stages.h",
                 "moe_transformer_layer_amd/csrc/dsl_device.h", "include/dsl.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            hsh.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            hsh.update(_code_only(f.read()).encode())
     return hsh.hexdigest()[:16]
 
 
