@@ -7,9 +7,11 @@ layer's weights in HBM (as a model holds distinct layers) and step i runs copy
 i mod L, so no step finds the previous one's weights in the 256 MB Infinity Cache.
 
 Prints one JSON line: the M=6 full layer (top-6 of 128 experts) as the headline,
-the M=48 layer as a second point, the roofline of the launch (algorithmic HBM
-bytes per step over the measured kernel time against 8 TB/s), and the CPU oracle
-timed on a bounded sample.
+the M=48 layer and the three chained draft layers at M=6 (top-3, per layer) as
+further points, the roofline of the launch (algorithmic HBM bytes per step over the
+measured kernel time against 8 TB/s, and against a plain device copy's measured
+rate), and the CPU oracle timed on a bounded sample.  Each point also gives the wall
+time per layer when the same launches are replayed from a captured HIP graph.
 """
 from __future__ import annotations
 
@@ -25,10 +27,11 @@ sys.path.insert(0, ROOT)
 PEAK_GBS = 8000.0  # MI355X HBM3E
 
 
-def algorithmic_bytes(d, M: int, ids, kv) -> dict:
-    """Bytes the step must move: every weight read once (each distinct selected expert
-    once), the KV records read (union of the rows' windows per request) and written,
-    and the activations in and out."""
+def algorithmic_bytes(d, M: int, layer_ids, kv) -> dict:
+    """Bytes one launch must move: every layer's weights read once (each distinct
+    selected expert once), the KV records read (the union of the rows' windows, or of
+    their index-table rows, per layer) and written, and the activations in and out.
+    layer_ids: the selected experts [n_layers][M][k]."""
     h, qr, D, HD, orr = d.hidden, d.q_rank, d.head_dim, d.n_heads * d.head_dim, d.o_rank
     E, I, Is = d.n_experts, d.inter, d.shared_inter
 
@@ -40,22 +43,28 @@ def algorithmic_bytes(d, M: int, ids, kv) -> dict:
     shared = 3 * h * Is + 4 * ((2 * Is // 128) * (h // 128) + (h // 128) * (Is // 128))
     per_expert = 3 * h * I // 2 + 3 * h * I // 32
     live = [i for i in range(M) if kv.positions[i] >= 0]
-    distinct = sorted({int(e) for i in live for e in ids[i]})
     rec = D + 16
     seen = set()
     for i in live:
-        p, q = int(kv.positions[i]), int(kv.row_req[i])
-        for t in range(max(0, p - d.window + 1), p + 1):
-            seen.add((q, t))
-    kv_read = len(seen) * rec
-    kv_write = len(live) * rec
+        if d.swa_width > 0:
+            seen.update(int(t) for t in kv.key_table[i] if t >= 0)
+        else:
+            p, q = int(kv.positions[i]), int(kv.row_req[i])
+            seen.update((q, t) for t in range(max(0, p - d.window + 1), p + 1))
+    kv_layer = len(seen) * rec + len(live) * rec
+    nl = d.n_layers
+    distinct = [len({int(e) for i in live for e in layer_ids[l][i]}) for l in range(nl)]
     act = 2 * M * h * 2
-    total = attn + router + shared + len(distinct) * per_expert + kv_read + kv_write + act
-    return dict(total=total, attention=attn, router=router, shared=shared, experts=len(distinct) * per_expert,
-                n_distinct=len(distinct), kv=kv_read + kv_write, act=act)
+    total = nl * (attn + router + shared + kv_layer) + sum(distinct) * per_expert + act
+    return dict(total=total, per_layer=total / nl, n_layers=nl, attention=attn, router=router, shared=shared,
+                experts=sum(distinct) * per_expert, n_distinct=distinct, kv=nl * kv_layer, act=act)
 
 
-def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup: int, weights, seed: int = 0):
+def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup: int, weights, seed: int = 0,
+              graph_replay: bool = True):
+    """Times `steps` launches of workload `name` at M rows, rotating over `layers_dev`
+    device copies of the weights, with HIP events on the launch stream; then replays the
+    same launches from a captured HIP graph for the launch-gap-free wall time."""
     from moe_transformer_layer_amd import synth
     case = synth.make_case(name, seed, M=M, layers=weights)
     d = case.dims
@@ -64,38 +73,54 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
     handles = [dev.handle]
     copies = []
     for _ in range(layers_dev - 1):
-        wd = {k: v.clone() for k, v in dev.w_dev[0].items()}
+        wd = [{k: v.clone() for k, v in lw.items()} for lw in dev.w_dev]
         copies.append(wd)
-        ws = dsl.Weights(**{k: wd[k].data_ptr() for k in dsl.WEIGHT_FIELDS})
-        handles.append(dsl.dsl_layer_build(dsl.dims_struct(d), [ws]))
+        ws = [dsl.Weights(**{k: lw[k].data_ptr() for k in dsl.WEIGHT_FIELDS}) for lw in wd]
+        handles.append(dsl.dsl_layer_build(dsl.dims_struct(d), ws))
     x = torch.from_numpy(case.x.view("int16")).to(dev.dev)
     out = torch.zeros_like(x)
-    ids = torch.zeros((M, d.top_k), dtype=torch.int32, device=dev.dev)
-    taps = dsl.Taps(None, None, None, None, ids.data_ptr(), None, None, None)
+    layer_ids = torch.zeros((d.n_layers, M, d.top_k), dtype=torch.int32, device=dev.dev)
+    taps = dsl.Taps(None, None, None, None, None, None, None, layer_ids.data_ptr())
     stream = dev.stream()
     for hnd in handles:
         dsl.dsl_layer_reserve(hnd, M)
     dsl.dsl_decode_step(handles[0], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(), out.data_ptr(),
                         taps, stream)
     torch.cuda.synchronize()
-    ids_h = ids.cpu().numpy()
+    ids_h = layer_ids.cpu().numpy()
 
-    def step(i):
+    def step(i, strm):
         dsl.dsl_decode_step(handles[i % len(handles)], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(),
-                            out.data_ptr(), None, stream)
+                            out.data_ptr(), None, strm)
 
     for i in range(warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        step(i)
+        step(i, stream)
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    wall_graph = None
+    if graph_replay:
+        # the same launches captured once and replayed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            for i in range(steps):
+                step(i, torch.cuda.current_stream().cuda_stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall_graph = (time.perf_counter() - t0) / reps
+        del graph
     for hnd in handles:
         rc = dsl.dsl_layer_health(hnd)
         if rc:
@@ -110,9 +135,33 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
     dev.close()
     del copies
     torch.cuda.empty_cache()
-    return dict(M=M, us_per_layer_wall=wall / steps * 1e6, us_kernel_mean=mean_us, us_kernel_p10=per[len(per) // 10],
+    nl = d.n_layers
+    return dict(M=M, n_layers=nl, us_per_layer_wall=wall / steps / nl * 1e6,
+                us_per_layer_graph=None if wall_graph is None else wall_graph / steps / nl * 1e6,
+                us_kernel_mean=mean_us,
+                us_per_layer_kernel=mean_us / nl, us_kernel_p10=per[len(per) // 10],
                 us_kernel_p50=per[len(per) // 2], us_kernel_p90=per[(9 * len(per)) // 10], gbs=gbs,
                 frac=gbs / PEAK_GBS, bytes=byts, grid=grid, n_weight_copies=len(handles))
+
+
+def copy_gbs(torch, mib: int = 1024, reps: int = 10) -> float:
+    """Read + write bytes per second of a plain device copy of `mib` MiB (torch's copy
+    kernel): the rate a plain stream reaches on this device, beside the 8 TB/s peak."""
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / t / 1e9
 
 
 def cpu_baseline(name: str, M: int, weights, seconds: float = 12.0) -> dict:
@@ -207,6 +256,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="distinct weight copies rotated for cold weights")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only-m6", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
@@ -225,13 +275,25 @@ def main():
     print("[bench] drawing the layer's weights", flush=True)
     weights = synth.make_weights("layer48", 7)
     print(f"[bench] M=6 full layer, {args.copies} weight copies, {args.steps} steps", flush=True)
-    m6 = run_point(dsl, torch, "layer48", 6, args.copies, args.steps, args.warmup, weights)
+    m6 = run_point(dsl, torch, "layer48", 6, args.copies, args.steps, args.warmup, weights,
+                   graph_replay=not args.no_graph)
     print(f"[bench] M=6: {m6['us_kernel_mean']:.1f} us/launch, {m6['gbs']:.0f} GB/s", flush=True)
     m48 = None
     if not args.only_m6:
         print("[bench] M=48 full layer", flush=True)
-        m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights)
+        m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
+                        graph_replay=not args.no_graph)
         print(f"[bench] M=48: {m48['us_kernel_mean']:.1f} us/launch, {m48['gbs']:.0f} GB/s", flush=True)
+    draft = None
+    if not args.only_m6:
+        # three chained draft layers in one launch; each layer's weights are a device copy
+        # of their own (of the same draw: the bytes streamed are what matters here)
+        print("[bench] M=6 draft layers (3 chained, index-table rows of 192, top-3)", flush=True)
+        draft = run_point(dsl, torch, "draft", 6, 2, args.steps, args.warmup, weights * 3,
+                          graph_replay=not args.no_graph)
+        print(f"[bench] draft M=6: {draft['us_per_layer_kernel']:.1f} us/layer, {draft['gbs']:.0f} GB/s", flush=True)
+    copy = copy_gbs(torch)
+    print(f"[bench] device copy: {copy:.0f} GB/s (read + write)", flush=True)
     cpu = None
     if not args.no_cpu:
         print("[bench] oracle cpu baseline", flush=True)
@@ -254,9 +316,11 @@ def main():
                                "cold weights", "rows": 6, "seq_context": "1k-64k paged, block 128"},
         "roofline": {"bound": "hbm", "achieved": round(m6["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(m6["frac"], 4), "traffic": measured_traffic(),
-                     "algorithmic_bytes": m6["bytes"]["total"], "kernel_us_mean": round(m6["us_kernel_mean"], 2)},
+                     "algorithmic_bytes": m6["bytes"]["total"], "kernel_us_mean": round(m6["us_kernel_mean"], 2),
+                     "copy_gbs": round(copy, 1), "frac_of_copy": round(m6["gbs"] / copy, 4)},
         "m6": m6,
         "m48": m48,
+        "draft_m6": draft,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

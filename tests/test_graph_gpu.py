@@ -1,0 +1,162 @@
+"""The decode launch under HIP-graph capture, and a race stress of its replays.
+
+Once a width has run eagerly on a handle (that first call allocates the width's
+scratch), a decode step is one kernel launch with its arguments passed by value: no
+allocation, no copy, no synchronous call.  A caller can therefore capture it in a HIP
+graph.  The grid barrier's counters only ever grow and each launch reads its starting
+value on entry, so replays need no reset.  Two widths on one handle use scratch of
+their own, and launches on one stream never overlap.
+
+Each test captures launches of two widths alternating on one handle, each width with
+its own cache, positions and input buffer.  Every launch writes an output slot and a set
+of intermediate taps of its own: attention output, residual, MoE input and output,
+expert ids and weights, router logits, every layer's ids.  Between replays the test does
+eager work of its own: it fills every buffer with a sentinel, switches the inputs
+between two sets, and synchronizes.  After every replay each launch's buffers must equal
+the eager launch on the same inputs bit for bit, and at the end the caches must hold what
+the eager launches wrote.
+
+  full-size layer (hidden 4096, top-6 of 128), widths 48 and 6:
+      a graph of 50 (48, 6) pairs replayed 1000 times = 100,000 launches
+  two chained draft layers (index-table mode) at small dims, widths 13 and 5:
+      a graph of 8 pairs replayed 40 times
+"""
+import numpy as np
+import pytest
+
+from moe_transformer_layer_amd import synth
+
+pytestmark = [pytest.mark.gpu]
+
+SENTINEL = 0x7FC1FFFF  # fill of the 32-bit buffers (a NaN; no id); the bf16 ones take -1 (0xFFFF, a NaN)
+
+
+def _say(msg):
+    print(f"[graph] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dsl(gpu):
+    from moe_transformer_layer_amd import dsl as d
+    d.lib()
+    return d
+
+
+class _Side:
+    """One width on the shared handle: its own cache, tables, inputs, and for every launch
+    in the graph an output slot and a set of intermediate taps of its own."""
+
+    def __init__(self, dsl, torch, name, layers, weights, layout, seed, pairs):
+        self.dsl, self.torch = dsl, torch
+        case = synth.make_case(name, seed, layers=layers, **layout)
+        d = case.dims
+        self.M = M = case.M
+        self.dev = dsl.LayerOnDevice(case, weights=weights)
+        rng = np.random.default_rng([seed, 77])
+        self.inputs = [torch.from_numpy(case.x.view(np.int16)).cuda(),
+                       torch.from_numpy(synth.gen_x(d, rng, M).view(np.int16)).cuda()]
+        self.x = torch.empty_like(self.inputs[0])
+        i16, i32 = torch.int16, torch.int32
+        # every buffer as raw integers: bit-for-bit compares, sentinel fills
+        self.shapes = dict(out=((M, d.hidden), i16), attn_out=((M, d.hidden), i16), hres=((M, d.hidden), i16),
+                           moe_in=((M, d.hidden), i16), moe_out=((M, d.hidden), i16), ids=((M, d.top_k), i32),
+                           w=((M, d.top_k), i32), logits=((M, d.n_experts), i32),
+                           layer_ids=((d.n_layers, M, d.top_k), i32))
+        self.slots = {k: torch.empty((pairs, *shp), dtype=dt, device="cuda") for k, (shp, dt) in self.shapes.items()}
+        self.ref = []
+
+    def launch(self, bufs):
+        dsl = self.dsl
+        taps = dsl.Taps(*(bufs[k].data_ptr() for k in ("attn_out", "hres", "moe_in", "moe_out", "ids", "w",
+                                                         "logits", "layer_ids")))
+        dsl.dsl_decode_step(self.dev.handle, self.x.data_ptr(), self.M, self.dev.kv_structs,
+                            self.dev.positions.data_ptr(), bufs["out"].data_ptr(), taps,
+                            self.torch.cuda.current_stream().cuda_stream)
+
+    def slot(self, j):
+        return {k: v[j] for k, v in self.slots.items()}
+
+    def select(self, i):
+        self.x.copy_(self.inputs[i])
+
+    def mismatches(self, i):
+        """Slots whose buffers differ from the eager launch on input set i, per buffer."""
+        bad = {}
+        for k, v in self.slots.items():
+            same = (v == self.ref[i][k]).flatten(1).all(dim=1)
+            if not bool(same.all()):
+                bad[k] = [j for j in range(v.shape[0]) if not bool(same[j])][:8]
+        return bad
+
+
+def _stress(dsl, name, layouts, pairs, replays, wseed=5):
+    """layouts: one make_case row layout per width (requests x rows per request + pad rows)."""
+    import torch
+    layers = synth.make_weights(name, wseed)
+    weights = dsl.DeviceWeights(synth.CONFIGS[name], layers)
+    sides = [_Side(dsl, torch, name, layers, weights, lay, 100 + j, pairs) for j, lay in enumerate(layouts)]
+    widths = tuple(s.M for s in sides)
+    # eager runs: each width once per input set (the first call allocates the width's scratch)
+    for i in range(2):
+        for s in sides:
+            s.select(i)
+            bufs = {k: torch.full(shp, SENTINEL, dtype=dt, device="cuda") if dt == torch.int32
+                    else torch.full(shp, -1, dtype=dt, device="cuda") for k, (shp, dt) in s.shapes.items()}
+            s.launch(bufs)
+            s.ref.append(bufs)
+    torch.cuda.synchronize()
+    dsl._check(dsl.dsl_layer_health(weights.handle))
+    caches_ref = [[c.clone() for c in s.dev.caches] for s in sides]  # after input set 1
+    for s in sides:
+        assert not torch.equal(s.ref[0]["out"], s.ref[1]["out"])
+        for i in range(2):
+            for k, v in s.ref[i].items():
+                assert not (v == (SENTINEL if v.dtype == torch.int32 else -1)).all(), f"eager launch left {k} unwritten"
+
+    graph = torch.cuda.CUDAGraph()
+    capture = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=capture):
+        for j in range(pairs):
+            for s in sides:
+                s.launch(s.slot(j))
+    _say(f"{name}: captured {pairs} x {widths}; {replays} replays = {replays * pairs * len(sides)} launches, "
+         f"{len(sides[0].slots)} buffers compared per launch")
+
+    bad = []
+    for r in range(replays):
+        i = r % 2
+        for s in sides:
+            for v in s.slots.values():
+                v.fill_(SENTINEL if v.dtype == torch.int32 else -1)
+            s.select(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in sides:
+            m = s.mismatches(i)
+            if m:
+                bad.append((r, s.M, m))
+        if bad:
+            break
+        if (r + 1) % 200 == 0:
+            _say(f"{name}: {r + 1} replays bit-exact")
+    dsl._check(dsl.dsl_layer_health(weights.handle))
+    assert not bad, f"replays that differ from the eager launch (replay, width, buffer: first slots): {bad[:4]}"
+    assert (replays - 1) % 2 == 1, "the last replay must use input set 1 for the cache check"
+    for s, refs in zip(sides, caches_ref):
+        for c, cr in zip(s.dev.caches, refs):
+            assert torch.equal(c, cr), f"width {s.M}: cache differs from the eager launches'"
+    del graph
+    for s in sides:
+        s.dev.close()
+    weights.close()
+
+
+def test_graph_draft_small(dsl):
+    _stress(dsl, "mid_draft", (dict(n_req=2, rows_per_req=6, n_pad=1), dict(n_req=1, rows_per_req=5)),
+            pairs=8, replays=40)
+
+
+@pytest.mark.timeout(600)
+def test_graph_race_stress_full(dsl):
+    _stress(dsl, "layer48", (dict(M=48), dict(M=6)), pairs=50, replays=1000)
