@@ -298,20 +298,25 @@ __device__ __forceinline__ unsigned barrier_base(SyncWords *sw) {
   return __hip_atomic_load(gptr(&sw->release[blockIdx.x & 7u][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// All blocks of the launch meet here.  Each wave first waits for its own memory
-// operations (its write-through stores are then at the device's coherence point), the
-// block meets, and thread 0 arrives with relaxed atomics.  Arrivals are counted in two
+// All blocks of the launch meet here, in two parts.  barrier_drain: each wave waits for
+// its own memory operations (its write-through stores are then at the device's
+// coherence point).  A wave may then issue loads that do not depend on the stage before
+// (the next stage's weights) and keep them in flight across the meeting.
+// grid_barrier_meet: the block meets (no wait on vector memory), and one thread, `bt`,
+// arrives with relaxed atomics; it must belong to a wave with no loads in flight, since
+// the atomics' results are waited for in issue order.  Arrivals are counted in two
 // levels (8 group counters, then one top counter) so no single address takes more than
 // nblocks/8 atomics; the last arrival writes the barrier's number into one release word
 // per group, and each group polls its own word, so the polls do not queue behind the
-// counters' atomics.  *next (thread 0's, in LDS) is the number this barrier completes.
+// counters' atomics.  *next (thread bt's, in LDS) is the number this barrier completes.
 // No cache maintenance: see stg.  The spin is bounded: a barrier that does not complete
 // records kFaultBarrier in the health word and lets the block go on, so the launch
 // always drains.
-__device__ __forceinline__ void grid_barrier(SyncWords *sw, unsigned nblocks, unsigned *next) {
-  __builtin_amdgcn_s_waitcnt(0);
+__device__ __forceinline__ void barrier_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ void grid_barrier_meet(SyncWords *sw, unsigned nblocks, unsigned *next, unsigned bt) {
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == bt) {
     const unsigned grp = blockIdx.x & 7u;
     const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
     const unsigned per = (nblocks - grp + 7u) / 8u;  // blocks in this group

@@ -1113,13 +1113,21 @@ struct Tracer {
   }
 };
 
-#define SYNC()                \
+// The grid barrier's thread is the first of the last wave: linear_prefetch leaves that
+// wave without loads in flight.  SYNC_PF issues the next stage's weight loads (ISSUE)
+// between the drain and the meeting.
+constexpr unsigned kBarrierThread = kThreads - kWave;
+
+#define SYNC_PF(ISSUE)        \
   do {                        \
     __syncthreads();          \
     tr.mark();                \
-    grid_barrier(sw, nb, &bar_next); \
+    barrier_drain();          \
+    ISSUE;                    \
+    grid_barrier_meet(sw, nb, &bar_next, kBarrierThread); \
     tr.mark();                \
   } while (0)
+#define SYNC() SYNC_PF((void)0)
 
 #define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
   const dsl_kv &kv = A_.kv; const Ctx cx = make_ctx(); (void)p; (void)w; (void)kv; (void)cx
@@ -1141,16 +1149,22 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     sw = kp->sync;
     tr.buf = kp->trace;
   }
-  // the last wave reads the barrier base: it has no work on the first stage's critical
-  // path (the first barrier's __syncthreads publishes the value to thread 0)
-  if (tid() == kThreads - kWave) bar_next = barrier_base(sw) + 1u;
+  // the barrier's thread reads the barrier base (the last wave has no work on the first
+  // stage's critical path)
+  if (tid() == kBarrierThread) bar_next = barrier_base(sw) + 1u;
   const bool moe_mode = mode == kModeMoe;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
     const bool last = l == n_layers - 1;
     if (!moe_mode) {
+      // The first weights of wqkv, wq_b, wo_a and wo_b are loaded between the drain and
+      // the grid barrier before them (SYNC_PF), at addresses taken at the start of the
+      // stage before, when its launch parameters are at hand.
+      PreA pf_wqkv = pre_none();
+      PreAddr pa;
       {
         STAGE(l);
+        pa = linear_prefetch_addr<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv);
         const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
           case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
@@ -1160,24 +1174,28 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_attn_norm_e<16>(p, w, kv, xin, red); break;
         }
       }
-      SYNC();
+      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
       {
         STAGE(l);
-        linear_all<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv);
+        linear_all_pre<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv, pf_wqkv);
       }
       SYNC();
+      PreA pf_wq_b = pre_none();
       {
         STAGE(l);
+        pa = linear_prefetch_addr<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb);
         st_qkv_post(p, w, kv, red, &wave_lds[0][0]);
       }
-      SYNC();
+      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
       {
         STAGE(l);
-        linear_all<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q);
+        linear_all_pre<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q, pf_wq_b);
       }
       SYNC();
+      PreA pf_wo_a = pre_none();
       {
         STAGE(l);
+        pa = linear_prefetch_addr<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa);
         float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
         switch (p.D) {
           case 64: st_attention_v<1>(p, cx, kv, lds); break;
@@ -1186,14 +1204,16 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_attention_v<8>(p, cx, kv, lds); break;
         }
       }
-      SYNC();
+      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
       {
         STAGE(l);
-        linear_all<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t);
+        linear_all_pre<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t, pf_wo_a);
       }
       SYNC();
+      PreA pf_wo_b = pre_none();
       {
         STAGE(l);
+        pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
         switch (row_elems(p.orr)) {
           case 1: st_t_quant_e<1>(p); break;
           case 2: st_t_quant_e<2>(p); break;
@@ -1202,10 +1222,10 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           default: st_t_quant_e<16>(p); break;
         }
       }
-      SYNC();
+      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_b));
       {
         STAGE(l);
-        linear_all<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a);
+        linear_all_pre<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a, pf_wo_b);
       }
       SYNC();
       {

@@ -252,6 +252,16 @@ __device__ __forceinline__ void step_mfma(const v4u af[NT][4], const float bsc[N
   }
 }
 
+// The weight bytes of the first 4 K steps of a wave's first task of a dense linear,
+// loaded ahead of the stage: after the previous stage's stores have drained and before
+// the grid barrier, so their HBM latency overlaps the barrier.  (The scales are loaded
+// with the activations after the barrier.)  on: the wave has such a task and it takes
+// the pipelined path (wave-uniform).
+struct PreA {
+  RawA ra[4];
+  bool on;
+};
+
 // NT weight tiles of 16 rows times NCG groups of 16 bf16 activation rows over `nsteps`
 // 128-wide K steps, software-pipelined in groups of 4 steps: ring buffers hold the raw
 // weight bytes and the activation fragments of the next 4 steps and the scales of the
@@ -260,9 +270,11 @@ __device__ __forceinline__ void step_mfma(const v4u af[NT][4], const float bsc[N
 // and 16-byte aligned scale rows.  kb = this lane's first activation K index.
 // acc[tt][c] lane l ends holding C[4*(l/16) + r][l%16]: weight row n0[tt] + 4*(l/16) + r,
 // activation row 16c + l%16.
+// With `use` (one tile only) the first group's weight bytes come from *pf.
 template <int FMT, int NT, int NCG>
 __device__ __forceinline__ void tiles_pipe4(const WStream ws[NT], int nsteps, const uint16_t *const xrow[NCG],
-                                            const bool xok[NCG], int kb, int g, v4f acc[NT][NCG]) {
+                                            const bool xok[NCG], int kb, int g, v4f acc[NT][NCG],
+                                            const PreA *pf = nullptr, bool use = false) {
   constexpr int P = 4;
   constexpr int PB = NCG == 1 ? 4 : (NCG == 2 ? 2 : 1);  // activation ring depth (16 registers per step and group)
   RawA ra[P][NT];
@@ -273,10 +285,15 @@ __device__ __forceinline__ void tiles_pipe4(const WStream ws[NT], int nsteps, co
     scg[tt] = load_scales4<FMT>(ws[tt], 0);
     if (nsteps > P) scn[tt] = load_scales4<FMT>(ws[tt], P);
   }
+  if (NT == 1 && use) {
 #pragma unroll
-  for (int j = 0; j < P; j++) {
+    for (int j = 0; j < P; j++) ra[j][0] = pf->ra[j];
+  } else {
 #pragma unroll
-    for (int tt = 0; tt < NT; tt++) load_a<FMT>(ra[j][tt], ws[tt], j);
+    for (int j = 0; j < P; j++) {
+#pragma unroll
+      for (int tt = 0; tt < NT; tt++) load_a<FMT>(ra[j][tt], ws[tt], j);
+    }
   }
 #pragma unroll
   for (int j = 0; j < PB; j++) {
@@ -337,16 +354,22 @@ __device__ __forceinline__ void tiles_pipe1(const WStream ws[NT], int nsteps, co
   }
 }
 
-// Pipelined path when the step count and scale alignment allow it, else the simple one.
+template <int FMT>
+__device__ __forceinline__ bool scales_aligned(const WStream &ws) {
+  return FMT == kW8B128 ? ((uintptr_t)ws.s32 & 15) == 0 : ((uintptr_t)ws.s8 & 15) == 0;
+}
+
+// Pipelined path when the step count and scale alignment allow it (always so when the
+// first group was loaded ahead, `use`), else the simple one.
 template <int FMT, int NT, int NCG>
 __device__ __forceinline__ void tiles(const WStream ws[NT], int nsteps, const uint16_t *const xrow[NCG],
-                                      const bool xok[NCG], int kb, int g, v4f acc[NT][NCG]) {
+                                      const bool xok[NCG], int kb, int g, v4f acc[NT][NCG],
+                                      const PreA *pf = nullptr, bool use = false) {
   bool fast = nsteps % 4 == 0;
 #pragma unroll
-  for (int tt = 0; tt < NT; tt++)
-    fast = fast && (FMT == kW8B128 ? ((uintptr_t)ws[tt].s32 & 15) == 0 : ((uintptr_t)ws[tt].s8 & 15) == 0);
+  for (int tt = 0; tt < NT; tt++) fast = fast && scales_aligned<FMT>(ws[tt]);
   if (fast)
-    tiles_pipe4<FMT, NT, NCG>(ws, nsteps, xrow, xok, kb, g, acc);
+    tiles_pipe4<FMT, NT, NCG>(ws, nsteps, xrow, xok, kb, g, acc, pf, use);
   else
     tiles_pipe1<FMT, NT, NCG>(ws, nsteps, xrow, xok, kb, g, acc);
 }
@@ -356,7 +379,8 @@ __device__ __forceinline__ void tiles(const WStream ws[NT], int nsteps, const ui
 // so each gets its own register allocation.
 template <int FMT, int NCG>
 __device__ __forceinline__ void linear_task_n(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32,
-                                           int N, int K, int kc, const uint16_t *x, int M, float *part) {
+                                           int N, int K, int kc, const uint16_t *x, int M, float *part,
+                                           const PreA *pf, bool use) {
   const int ntile = N >> 4;
   const int ks = t / ntile, nt = t - ks * ntile;
   const int i = lane & 15, g = lane >> 4;
@@ -373,7 +397,7 @@ __device__ __forceinline__ void linear_task_n(int t, int lane, const uint8_t *W,
     xrow[c] = x + (size_t)(xok[c] ? m : 0) * K;
     acc[0][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  tiles<FMT, 1, NCG>(ws, kc >> 7, xrow, xok, k0 + 32 * g, g, acc);
+  tiles<FMT, 1, NCG>(ws, kc >> 7, xrow, xok, k0 + 32 * g, g, acc, pf, use);
 #pragma unroll
   for (int c = 0; c < NCG; c++) {
     const int m = 16 * c + i;
@@ -383,21 +407,78 @@ __device__ __forceinline__ void linear_task_n(int t, int lane, const uint8_t *W,
 
 template <int FMT>
 __device__ __forceinline__ void linear_task(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32,
-                                            int N, int K, int kc, const uint16_t *x, int M, float *part) {
+                                            int N, int K, int kc, const uint16_t *x, int M, float *part,
+                                            const PreA *pf = nullptr, bool use = false) {
   const int ncg = (M + 15) >> 4;
   if (ncg == 1)
-    linear_task_n<FMT, 1>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+    linear_task_n<FMT, 1>(t, lane, W, S8, S32, N, K, kc, x, M, part, pf, use);
   else if (ncg == 2)
-    linear_task_n<FMT, 2>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+    linear_task_n<FMT, 2>(t, lane, W, S8, S32, N, K, kc, x, M, part, pf, use);
   else
-    linear_task_n<FMT, 3>(t, lane, W, S8, S32, N, K, kc, x, M, part);
+    linear_task_n<FMT, 3>(t, lane, W, S8, S32, N, K, kc, x, M, part, pf, use);
 }
 
+// Task t of a dense linear to global wave t mod waves.
 template <int FMT>
 __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N, int K, int kc,
                            const uint16_t *x, int M, float *part) {
   const int T = (N >> 4) * (K / kc);
   for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+}
+
+// The same, the wave's first task starting from the weights linear_prefetch loaded.
+template <int FMT>
+__device__ __forceinline__ void linear_all_pre(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N,
+                                               int K, int kc, const uint16_t *x, int M, float *part, const PreA &pf) {
+  const int T = (N >> 4) * (K / kc);
+  int t = cx.gw;
+  if (t < T) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part, &pf, pf.on);
+  // (the first task peeled: pf is dead after it)
+  for (t += cx.nw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+}
+
+// Where this wave's first task of linear_all_pre (same arguments) starts, when it has
+// one, takes the pipelined path and is not in the last wave (which holds the grid
+// barrier's thread and so must have no loads in flight).  Computed before the drain, so
+// that only the loads themselves come between the drain and the barrier.
+struct PreAddr {
+  WStream ws;
+  bool on;
+};
+
+template <int FMT>
+__device__ __forceinline__ PreAddr linear_prefetch_addr(const Ctx &cx, const uint8_t *W, const uint8_t *S8,
+                                                        const float *S32, int N, int K, int kc) {
+  const int ntile = N >> 4, T = ntile * (K / kc), t = cx.gw, nsteps = kc >> 7;
+  PreAddr a;
+  const int tc = t < T ? t : 0;
+  const int ks = tc / ntile, nt = tc - ks * ntile, i = cx.lane & 15, g = cx.lane >> 4;
+  a.ws = wstream<FMT>(W, S8, S32, K, nt * 16 + i, ks * kc, g);
+  a.on = t < T && cx.wave != kWavesPerBlock - 1 && nsteps % 4 == 0 && scales_aligned<FMT>(a.ws);
+  return a;
+}
+
+// No prefetched weights.  Every field is set, so no earlier value stays live across the
+// layer loop; the register fields take arbitrary values (no instructions, and no join
+// that would have to wait for a load).
+__device__ __forceinline__ PreA pre_none() {
+  PreA pf;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    pf.ra[j].a0 = __builtin_nondeterministic_value(pf.ra[j].a0);
+    pf.ra[j].a1 = __builtin_nondeterministic_value(pf.ra[j].a1);
+  }
+  pf.on = false;
+  return pf;
+}
+
+// Loads the weight bytes of the first group of the task at a into pf.
+template <int FMT>
+__device__ __forceinline__ void linear_prefetch(const PreAddr &a, PreA &pf) {
+  if (!a.on) return;
+  pf.on = true;
+#pragma unroll
+  for (int j = 0; j < 4; j++) load_a<FMT>(pf.ra[j], a.ws, j);
 }
 
 // ============================================================== block-level helpers

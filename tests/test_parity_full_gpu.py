@@ -37,6 +37,7 @@ Tolerances beyond the common bf16 bar, and why:
   outputs are compared on the rows whose routing matched in every layer.
 """
 import dataclasses
+import time
 
 import numpy as np
 import pytest
@@ -55,8 +56,11 @@ G_DRIFT = 1e-2
 SEEDS = load_seeds()
 
 
+_T0 = time.perf_counter()
+
+
 def _say(msg):
-    print(f"[parity-full] {msg}", flush=True)
+    print(f"[parity-full +{time.perf_counter() - _T0:.0f}s] {msg}", flush=True)
 
 
 @pytest.fixture(scope="module")
@@ -118,6 +122,7 @@ def _case_and_oracle(dsl, name, key):
     sd = _seeded(key)
     layers, dw = _device_weights(dsl, name, sd["weights_seed"])
     case = synth.make_case(name, sd["seed"], M=sd["M"], layers=layers)
+    _say(f"{key}: oracle, {case.dims.n_layers} layer(s) at M={case.M}")
     res, caches = oracle_decode(case)
     live = decode_live(case)
     g = min_gap(case.dims, res["layers"], live)
@@ -188,6 +193,7 @@ def _run_chain(dsl, name, key):
         s.close()
 
     # 3. the fused chain against the oracle's chain
+    _say(f"{key}: fused chain against the oracle's chain")
     ok = live.copy()
     for l in range(L):
         want = res["layers"][l]
