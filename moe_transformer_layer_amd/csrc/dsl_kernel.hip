@@ -391,6 +391,62 @@ __device__ __forceinline__ void st_t_quant_e(const Params &p) {
   }
 }
 
+// t_quant folded into wo_a.  The wo_a tasks of one 32-column group of t (one MX block
+// wide: 2 column tiles x the K chunks) count their finished tasks on a counter that only
+// grows; the task that finishes a group last sums the group's split-K partials and
+// quantizes them, as st_t_quant_e does (same helpers, same order), so no grid barrier and
+// row stage are needed between wo_a and wo_b.  Each task's partial stores are drained
+// before its count, so they are at the coherence point when the last task reads them
+// (the grid barrier's rule, with the counter in place of the barrier).  Used while every
+// wave has at most one wo_a task and M <= 16 (two passes of 8 rows for the last task);
+// `base` is the group's counter before the layer, read at the start of the launch.
+constexpr int kTqGroups = 64;
+
+__device__ __forceinline__ bool tq_fold(const Params &p) {
+  const int T = (p.orr >> 4) * ((p.H * p.D) / p.pl.kc_oa);
+  return p.M <= 16 && T <= (int)gridDim.x * kWavesPerBlock && p.orr / 32 <= kTqGroups;
+}
+
+// The group of this wave's wo_a task, or -1
+__device__ __forceinline__ int tq_group(const Params &p, const Ctx &cx) {
+  const int ntile = p.orr >> 4, T = ntile * ((p.H * p.D) / p.pl.kc_oa);
+  return cx.gw < T ? (cx.gw % ntile) >> 1 : -1;
+}
+
+// The last task of group j: t[m][32 j .. 32 j + 32) for every row m.  Lane l takes row
+// m0 + l / 8 and columns 32 j + 4 (l % 8) .. + 4; the 8 lanes of a row hold its block.
+__device__ __forceinline__ void tq_group_quant(const Params &p, int j, int lane) {
+  const int N = p.orr, nks = (p.H * p.D) / p.pl.kc_oa, k = 32 * j + 4 * (lane & 7);
+  for (int m0 = 0; m0 < p.M; m0 += 8) {
+    const int m = m0 + (lane >> 3);
+    float v[4];
+    if (m < p.M)
+      load_sum_f32<4>(p.s.p_t + (size_t)m * N + k, (size_t)p.M * N, nks, v);
+    else
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = 0.f;
+    mx_quant_dequant<4>(v);
+    if (m < p.M) store_bf16<4>(p.s.tb + (size_t)m * N + k, v);
+  }
+}
+
+__device__ __forceinline__ void st_wo_a_fold(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
+                                             unsigned base) {
+  const int N = p.orr, K = p.H * p.D, kc = p.pl.kc_oa, nks = K / kc, T = (N >> 4) * nks;
+  const int t = cx.gw;
+  if (t >= T) return;
+  linear_task<kW8T32>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t, &pf, pf.on);
+  const int j = tq_group(p, cx);
+  __builtin_amdgcn_s_waitcnt(0);  // this task's partials are at the coherence point
+  unsigned old = 0;
+  if (cx.lane == 0)
+    old = __hip_atomic_fetch_add(gptr(&p.sync->tq[j][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = (unsigned)__builtin_amdgcn_readfirstlane(old);
+  if (old - base != 2u * (unsigned)nks - 1u) return;
+  asm volatile("" ::: "memory");  // the partial loads stay after the count
+  tq_group_quant(p, j, cx.lane);
+}
+
 // wo_b output a (sum of partials).  Attention-only steps write bf16(a).  Full steps:
 // hres = bf16(x + a), u = bf16(RMSNorm_ffn(hres)).  Pad rows give zeros.
 template <int E>
@@ -1104,11 +1160,13 @@ __device__ __forceinline__ StageArgs stage_args(int l) {
 // With tracing on, every block stamps the device wall clock at the start of the
 // launch, on arriving at and on leaving every grid barrier, at a few points inside the
 // MoE and at the end: buf[mark][block].
+constexpr int kTraceMarks = 256;  // stamps per block the trace buffer holds
+
 struct Tracer {
   unsigned long long *buf = nullptr;
   int n = 0;
   __device__ __forceinline__ void mark() {
-    if (buf && tid() == 0) stg(buf + (size_t)n * gridDim.x + bid(), (unsigned long long)wall_clock64());
+    if (buf && tid() == 0 && n < kTraceMarks) stg(buf + (size_t)n * gridDim.x + bid(), (unsigned long long)wall_clock64());
     n++;
   }
 };
@@ -1137,7 +1195,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ Routing R;
   __shared__ float red[16];
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[kWavesPerBlock][4096];  // per-wave scale staging
-  __shared__ unsigned bar_next;  // number of the next grid barrier (thread 0's)
+  __shared__ unsigned bar_next;  // number of the next grid barrier (the barrier thread's)
+  __shared__ unsigned tq_base[kWavesPerBlock];  // each wave's wo_a group counter before this layer
   const unsigned nb = gridDim.x;
   int mode, n_layers;
   SyncWords *sw;
@@ -1165,6 +1224,14 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv);
+        if (l == 0 && cx.lane == 0) {
+          // before this block's first arrival, like the barrier base: no wo_a task of the
+          // launch can count before every block has arrived at the first barrier
+          const int j = tq_group(p, cx);
+          tq_base[cx.wave] = j >= 0 && j < kTqGroups
+                                 ? __hip_atomic_load(gptr(&p.sync->tq[j][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0u;
+        }
         const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
           case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
@@ -1205,26 +1272,38 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         }
       }
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
-      {
-        STAGE(l);
-        linear_all_pre<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t, pf_wo_a);
-      }
-      SYNC();
       PreA pf_wo_b = pre_none();
+      bool fold;
       {
         STAGE(l);
-        pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
-        switch (row_elems(p.orr)) {
-          case 1: st_t_quant_e<1>(p); break;
-          case 2: st_t_quant_e<2>(p); break;
-          case 4: st_t_quant_e<4>(p); break;
-          case 8: st_t_quant_e<8>(p); break;
-          default: st_t_quant_e<16>(p); break;
+        fold = tq_fold(p);
+        if (fold) {
+          pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
+          st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave]);
+        } else {
+          linear_all_pre<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t,
+                                 pf_wo_a);
+        }
+      }
+      if (!fold) {
+        SYNC();
+        {
+          STAGE(l);
+          pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
+          switch (row_elems(p.orr)) {
+            case 1: st_t_quant_e<1>(p); break;
+            case 2: st_t_quant_e<2>(p); break;
+            case 4: st_t_quant_e<4>(p); break;
+            case 8: st_t_quant_e<8>(p); break;
+            default: st_t_quant_e<16>(p); break;
+          }
         }
       }
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_b));
       {
         STAGE(l);
+        // (this wave's own slot, read in wo_a before the barrier)
+        if (fold && cx.lane == 0) tq_base[cx.wave] += 2u * (unsigned)((p.H * p.D) / p.pl.kc_oa);
         linear_all_pre<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a, pf_wo_b);
       }
       SYNC();
@@ -1325,7 +1404,7 @@ struct dsl_layer {
   WidthScratch wid[DSL_MAX_ROWS + 1];
 };
 
-static constexpr int kTraceLen = 256;
+static constexpr int kTraceLen = kTraceMarks;
 
 static thread_local std::string g_err;
 
