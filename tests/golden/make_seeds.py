@@ -28,6 +28,9 @@ CASES = {
     "layer48_m48": ("layer48", 7, dict(M=48), "decode"),
     "layer48_m6": ("layer48", 7, dict(M=6), "decode"),
     **{f"draft_m{m}": ("draft", 11, dict(M=m), "decode") for m in (1, 6, 12, 24, 36, 48)},
+    # either side of 16 rows (2 requests x (1 + 7 drafts), and one pad row more)
+    "draft_m16": ("draft", 11, dict(n_req=2, rows_per_req=8), "decode"),
+    "draft_m17": ("draft", 11, dict(n_req=2, rows_per_req=8, n_pad=1), "decode"),
 }
 
 

@@ -6,8 +6,10 @@ make_seeds.py with the oracle alone); each test re-checks the top-k gap rule.
   MoE stage alone, M = 6, top-3                 (moe6)
   attention half alone, M = 48 (8 x 6 rows)     (attn48)
   full layer, top-6, M = 48 and M = 6           (layer48)
-  three draft layers, 192-wide index rows, top-3, M in {1, 6, 12, 24, 36, 48}, one
-  handle for all widths (each width gets its own scratch)  (draft)
+  three draft layers, 192-wide index rows, top-3, M in {1, 6, 12, 16, 17, 24, 36, 48}
+  (16 = 2 requests x 8 rows, 17 the same and a pad row: either side of the widest step
+  whose wo_a output quantization is folded into wo_a), one handle for all widths (each
+  width gets its own scratch)  (draft)
 
 Tolerances beyond the common bf16 bar, and why:
 
@@ -121,7 +123,8 @@ def _check_layer(er: Errors, d, lw, got, want, live, got_cache, want_cache, befo
 def _case_and_oracle(dsl, name, key):
     sd = _seeded(key)
     layers, dw = _device_weights(dsl, name, sd["weights_seed"])
-    case = synth.make_case(name, sd["seed"], M=sd["M"], layers=layers)
+    layout = {k: sd[k] for k in ("M", "n_req", "rows_per_req", "n_pad") if k in sd}
+    case = synth.make_case(name, sd["seed"], layers=layers, **layout)
     _say(f"{key}: oracle, {case.dims.n_layers} layer(s) at M={case.M}")
     res, caches = oracle_decode(case)
     live = decode_live(case)
@@ -269,6 +272,6 @@ def test_full_layer_m6_top6(dsl):
     _run_decode(dsl, "layer48", "layer48_m6")
 
 
-@pytest.mark.parametrize("M", [1, 6, 12, 24, 36, 48])
+@pytest.mark.parametrize("M", [1, 6, 12, 16, 17, 24, 36, 48])
 def test_draft_three_layers(dsl, M):
     _run_chain(dsl, "draft", f"draft_m{M}")
