@@ -258,6 +258,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only-m6", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
+    ap.add_argument("--only-m48", action="store_true", help="only the M=48 layer (for counter passes)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
@@ -275,6 +276,12 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     print("[bench] drawing the layer's weights", flush=True)
     weights = synth.make_weights("layer48", 7)
+    if args.only_m48:
+        m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
+                        graph_replay=not args.no_graph)
+        print(f"[bench] M=48: {m48['us_kernel_mean']:.1f} us/launch, {m48['gbs']:.0f} GB/s", flush=True)
+        print(json.dumps({"m48": m48}), flush=True)
+        return
     print(f"[bench] M=6 full layer, {args.copies} weight copies, {args.steps} steps", flush=True)
     m6 = run_point(dsl, torch, "layer48", 6, args.copies, args.steps, args.warmup, weights,
                    graph_replay=not args.no_graph)
