@@ -64,8 +64,9 @@ def algorithmic_bytes(d, M: int, layer_ids, kv) -> dict:
 def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup: int, weights, seed: int = 0,
               graph_replay: bool = True):
     """Times `steps` launches of workload `name` at M rows, rotating over `layers_dev`
-    device copies of the weights, with HIP events on the launch stream; then replays the
-    same launches from a captured HIP graph for the launch-gap-free wall time."""
+    device copies of the weights: once for the wall time, once more with HIP events on
+    the launch stream around every launch for the kernel time; then replays the same
+    launches from a captured HIP graph for the launch-gap-free wall time."""
     from moe_transformer_layer_amd import synth
     case = synth.make_case(name, seed, M=M, layers=weights)
     d = case.dims
@@ -97,6 +98,14 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
     for i in range(warmup):
         step(i, stream)
     torch.cuda.synchronize()
+    # the wall time of the timed steps, with nothing else on the stream between launches
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the same steps again, each launch bracketed by HIP events: its kernel time
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -105,7 +114,7 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
         step(i, stream)
         ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_events = time.perf_counter() - t0
     wall_graph = None
     if graph_replay:
         # the same launches captured once and replayed
@@ -138,6 +147,7 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
     torch.cuda.empty_cache()
     nl = d.n_layers
     return dict(M=M, n_layers=nl, us_per_layer_wall=wall / steps / nl * 1e6,
+                us_per_layer_wall_with_events=wall_events / steps / nl * 1e6,
                 us_per_layer_graph=None if wall_graph is None else wall_graph / steps / nl * 1e6,
                 us_kernel_mean=mean_us,
                 us_per_layer_kernel=mean_us / nl, us_kernel_p10=per[len(per) // 10],
