@@ -286,6 +286,7 @@ struct SyncWords {
   unsigned top[64];         // groups fully arrived
   unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
   unsigned tq[64][16];      // wo_a tasks finished per 32-column group of t; only grow
+  unsigned cb[128][16];     // down-stage waves finished per 32-column group of the MoE output; only grow
   unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };

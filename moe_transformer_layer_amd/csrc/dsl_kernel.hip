@@ -1096,6 +1096,98 @@ __device__ __forceinline__ void st_combine_out(const Params &p, const Routing &R
   }
 }
 
+// The combine folded into the down stage (M <= 8).  Both loops of st_down hand task t to
+// wave t mod waves, and a task's 16 output columns are tile t mod (h / 16), so when the
+// tile count divides the wave count every task of a wave lies in the tile gw mod (h / 16).
+// Each wave drains its stores and counts once on the counter of its 32-column group (two
+// tiles: one 128-byte line of every partial row, so no line is read before its last
+// write); the wave that counts last combines the group's columns for every row, with
+// st_combine_out's arithmetic in its order, and no grid barrier and row stage are needed
+// between down and combine.  Every wave counts, with tasks or not, so a group takes
+// 2 * waves / (h / 16) counts per layer; `cb_base` holds each wave's group counter before
+// the layer, read at the start of the launch like the t_quant fold's.
+constexpr int kCbGroups = 128;
+
+__device__ __forceinline__ bool cb_fold(const Params &p) {
+  const int ntile = p.h >> 4, nw = (int)gridDim.x * kWavesPerBlock;
+  // (the last wave stores two bf16 columns at a time)
+  const bool al = ((uintptr_t)p.out & 3u) == 0 && ((uintptr_t)p.taps.moe_out & 3u) == 0;
+  return p.M <= 8 && (p.h & 31) == 0 && ntile > 0 && nw % ntile == 0 && (p.h >> 5) <= kCbGroups && al;
+}
+
+__device__ __forceinline__ int cb_group(const Params &p, const Ctx &cx) { return (cx.gw % (p.h >> 4)) >> 1; }
+
+// The last wave of group g: columns 32 g .. 32 g + 32 of every row.  Lane l takes columns
+// 32 g + 2 (l % 16) and + 1 of rows l / 16 and l / 16 + 4; live[i] is row l / 16 + 4 i's.
+__device__ __forceinline__ void cb_group_combine(const Params &p, const Routing &R, bool moe_mode, bool last,
+                                                 uint16_t *dst, int g, int lane, const bool live[2]) {
+  const int h = p.h, k = p.k, nks = p.Is / p.pl.kc_shd;
+  const size_t pstride = (size_t)p.M * h;
+  const int n = 32 * g + 2 * (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int m = (lane >> 4) + 4 * i;
+    if (m >= p.M) continue;
+    const size_t idx = (size_t)m * h + n;
+    float mo[2] = {0.f, 0.f};
+    uint32_t hr = 0;
+    if (live[i]) {
+      float2 yv[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) yv[j] = j < k ? ld_f2(p.s.y + (size_t)R.pair[m * k + j] * h + n) : make_float2(0.f, 0.f);
+      if (!moe_mode) hr = ldg(reinterpret_cast<const uint32_t *>(p.s.hres + idx));
+      load_sum_f32<2>(p.s.p_shd + idx, pstride, nks, mo);
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (j < k) {
+          const float wj = R.w[m * k + j];
+          mo[0] = fmaf(wj, yv[j].x, mo[0]);
+          mo[1] = fmaf(wj, yv[j].y, mo[1]);
+        }
+    }
+    const uint32_t mob = live[i] ? f32_to_bf16(mo[0]) | (f32_to_bf16(mo[1]) << 16) : 0u;
+    if (moe_mode) {
+      stg(reinterpret_cast<uint32_t *>(dst + idx), mob);
+    } else {
+      const uint32_t ob = live[i] ? f32_to_bf16(bf16_to_f32(hr & 0xFFFFu) + mo[0]) |
+                                        (f32_to_bf16(bf16_to_f32(hr >> 16) + mo[1]) << 16)
+                                  : 0u;
+      stg(reinterpret_cast<uint32_t *>(dst + idx), ob);
+      if (last && p.taps.moe_out) stg(reinterpret_cast<uint32_t *>((uint16_t *)p.taps.moe_out + idx), mob);
+    }
+  }
+}
+
+// After this wave's st_down tasks
+__device__ __forceinline__ void cb_count_combine(const Params &p, const Ctx &cx, const Routing &R, bool moe_mode,
+                                                 bool last, uint16_t *dst, unsigned *cb_base) {
+  const int g = cb_group(p, cx);
+  const unsigned per = 2u * (unsigned)(cx.nw / (p.h >> 4));
+  const unsigned base = cb_base[cx.wave];
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's y and partial stores are at the coherence point
+  unsigned old = 0;
+  if (cx.lane == 0)
+    old = __hip_atomic_fetch_add(gptr(&p.sync->cb[g][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = (unsigned)__builtin_amdgcn_readfirstlane(old);
+  if (cx.lane == 0) cb_base[cx.wave] = base + per;  // (this wave's own slot)
+  if (old - base != per - 1u) return;
+  asm volatile("" ::: "memory");  // the group's loads stay after the count
+  bool live[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int m = (cx.lane >> 4) + 4 * i;
+    live[i] = moe_mode || (m < p.M && ldg(p.pos + m) >= 0);
+  }
+  cb_group_combine(p, R, moe_mode, last, dst, g, cx.lane, live);
+}
+
+// Each wave's combine group counter, read before its block's first arrival (no down wave
+// of the launch can count before every block has arrived at the first barrier)
+__device__ __forceinline__ unsigned cb_read_base(const Params &p, const Ctx &cx) {
+  return cb_fold(p) ? __hip_atomic_load(gptr(&p.sync->cb[cb_group(p, cx)][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0u;
+}
+
 // ============================================================== the persistent launch
 
 // Launch parameters are read per stage through the constant address space: the empty
@@ -1197,6 +1289,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[kWavesPerBlock][4096];  // per-wave scale staging
   __shared__ unsigned bar_next;  // number of the next grid barrier (the barrier thread's)
   __shared__ unsigned tq_base[kWavesPerBlock];  // each wave's wo_a group counter before this layer
+  __shared__ unsigned cb_base[kWavesPerBlock];  // each wave's combine group counter before this layer
   const unsigned nb = gridDim.x;
   int mode, n_layers;
   SyncWords *sw;
@@ -1231,6 +1324,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           tq_base[cx.wave] = j >= 0 && j < kTqGroups
                                  ? __hip_atomic_load(gptr(&p.sync->tq[j][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : 0u;
+          cb_base[cx.wave] = cb_read_base(p, cx);
         }
         const uint16_t *xin = A_.xin;
         switch (row_elems(p.h)) {
@@ -1326,6 +1420,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     }
     {
       STAGE(l);
+      // (a MoE step's first stage: before this block's first arrival)
+      if (moe_mode && l == 0 && cx.lane == 0) cb_base[cx.wave] = cb_read_base(p, cx);
       st_router_shared(p, cx, w, moe_mode ? p.x : p.s.u);
     }
     SYNC();
@@ -1362,14 +1458,19 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       st_shared_swiglu(p, moe_mode);
     }
     SYNC();
+    bool cfold;
     {
       STAGE(l);
+      cfold = cb_fold(p);
       st_down(p, cx, w, R, wave_lds[cx.wave]);
+      if (cfold) cb_count_combine(p, cx, R, moe_mode, last, A_.xout, cb_base);
     }
-    SYNC();
-    {
-      STAGE(l);
-      st_combine_out(p, R, moe_mode, last, A_.xout);
+    if (!cfold) {
+      SYNC();
+      {
+        STAGE(l);
+        st_combine_out(p, R, moe_mode, last, A_.xout);
+      }
     }
     if (!last) {
       SYNC();

@@ -63,8 +63,10 @@ def test_tiny_layer_m1(dsl):
 
 
 # M = 8 and 9 sit on either side of the width up to which every block selects the experts
-# itself (no grid barrier before the routing)
-@pytest.mark.parametrize("n_req,rows,n_pad", [(2, 6, 1), (1, 5, 0), (3, 4, 0), (2, 4, 0), (1, 8, 1)])
+# itself (no grid barrier before the routing) and up to which the down stage's last wave
+# per column group combines (no grid barrier before the combine); 1x6+1 and 2x3+2 put pad
+# rows in that folded combine
+@pytest.mark.parametrize("n_req,rows,n_pad", [(2, 6, 1), (1, 5, 0), (3, 4, 0), (2, 4, 0), (1, 8, 1), (1, 6, 1), (2, 3, 2)])
 def test_mid_layer_ragged(dsl, n_req, rows, n_pad):
     case, (res, caches) = _decode_case("mid", f"mid_{n_req}x{rows}+{n_pad}", first=100,
                                        n_req=n_req, rows_per_req=rows, n_pad=n_pad)
