@@ -133,3 +133,30 @@ def test_repeat_launch_bit_exact(dsl):
         dev.close()
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_modes_and_widths_interleaved_bit_exact(dsl):
+    """Decode, MoE-only and attention-only steps of two widths, interleaved on one handle,
+    each give what it gave when it ran first.  Steps of up to 8 rows finish the MoE on
+    counters in the handle's sync words whose starting values every launch reads for
+    itself (in its first stage, whatever the step's kind); a 12-row step does not count on
+    them, an attention-only step stops before them."""
+    d = synth.CONFIGS["mid"]
+    layers = synth.make_weights("mid", 3)
+    weights = dsl.DeviceWeights(d, layers)
+    small = dsl.LayerOnDevice(synth.make_case("mid", 700, layers=layers, n_req=1, rows_per_req=6, n_pad=1),
+                              weights=weights)
+    wide = dsl.LayerOnDevice(synth.make_case("mid", 701, layers=layers, n_req=2, rows_per_req=6), weights=weights)
+    u = synth.gen_x(d, np.random.default_rng(702), 7)
+    try:
+        steps = {"decode7": lambda: small.decode(small.case.x), "moe7": lambda: small.moe(u),
+                 "attn7": lambda: small.attn(small.case.x), "decode12": lambda: wide.decode(wide.case.x)}
+        first = {k: f() for k, f in steps.items()}
+        for k in ("moe7", "decode7", "decode12", "decode7", "attn7", "moe7", "decode7", "moe7"):
+            got = steps[k]()
+            for key in got:
+                assert np.array_equal(got[key], first[k][key]), f"{k}: {key} differs from its first run"
+    finally:
+        small.close()
+        wide.close()
+        weights.close()
