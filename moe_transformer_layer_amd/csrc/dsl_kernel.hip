@@ -175,9 +175,11 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 }
 
 // tmp: LDS of at least head_dim bytes for the record's codes
+// NARROW: the narrow-step kernel (q rank 1024, head dim 512: 2 and 1 elements per thread)
+template <bool NARROW>
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
                                             uint8_t *tmp) {
-  const int eq = row_elems(p.qr), ekv = row_elems(p.D);
+  const int eq = NARROW ? 2 : row_elems(p.qr), ekv = NARROW ? 1 : row_elems(p.D);
   // q of row m on block m, kv of row m on block M + m, row m's key offsets on block 2 M + m
   // (with fewer than 3 M blocks the key offsets come from the norm stage, with fewer than
   // 2 M all of a row's work is block m's)
@@ -186,31 +188,43 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
     if (b >= 2 * p.M && b < 3 * p.M) key_offsets_row(p, kv, b - 2 * p.M);
     if (b < p.M) {
       switch (eq) {
-        case 1: qpost_row<1>(p, w, b, red); break;
         case 2: qpost_row<2>(p, w, b, red); break;
-        case 4: qpost_row<4>(p, w, b, red); break;
-        case 8: qpost_row<8>(p, w, b, red); break;
-        default: qpost_row<16>(p, w, b, red); break;
+        default:
+          if constexpr (!NARROW) {
+            if (eq == 1) qpost_row<1>(p, w, b, red);
+            else if (eq == 4) qpost_row<4>(p, w, b, red);
+            else if (eq == 8) qpost_row<8>(p, w, b, red);
+            else qpost_row<16>(p, w, b, red);
+          }
+          break;
       }
     } else if (b < 2 * p.M) {
       switch (ekv) {
         case 1: kvpost_row<1>(p, w, kv, b - p.M, red, tmp); break;
-        default: kvpost_row<2>(p, w, kv, b - p.M, red, tmp); break;
+        default:
+          if constexpr (!NARROW) kvpost_row<2>(p, w, kv, b - p.M, red, tmp);
+          break;
       }
     }
     return;
   }
   for (int m = bid(); m < p.M; m += gridDim.x) {
     switch (eq) {
-      case 1: qpost_row<1>(p, w, m, red); break;
       case 2: qpost_row<2>(p, w, m, red); break;
-      case 4: qpost_row<4>(p, w, m, red); break;
-      case 8: qpost_row<8>(p, w, m, red); break;
-      default: qpost_row<16>(p, w, m, red); break;
+      default:
+        if constexpr (!NARROW) {
+          if (eq == 1) qpost_row<1>(p, w, m, red);
+          else if (eq == 4) qpost_row<4>(p, w, m, red);
+          else if (eq == 8) qpost_row<8>(p, w, m, red);
+          else qpost_row<16>(p, w, m, red);
+        }
+        break;
     }
     switch (ekv) {
       case 1: kvpost_row<1>(p, w, kv, m, red, tmp); break;
-      default: kvpost_row<2>(p, w, kv, m, red, tmp); break;
+      default:
+        if constexpr (!NARROW) kvpost_row<2>(p, w, kv, m, red, tmp);
+        break;
     }
   }
 }
@@ -435,7 +449,7 @@ __device__ __forceinline__ void st_wo_a_fold(const Params &p, const Ctx &cx, con
   const int N = p.orr, K = p.H * p.D, kc = p.pl.kc_oa, nks = K / kc, T = (N >> 4) * nks;
   const int t = cx.gw;
   if (t >= T) return;
-  linear_task<kW8T32>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t, &pf, pf.on);
+  linear_task<kW8T32, 1>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t, &pf, pf.on);
   const int j = tq_group(p, cx);
   __builtin_amdgcn_s_waitcnt(0);  // this task's partials are at the coherence point
   unsigned old = 0;
@@ -548,6 +562,7 @@ __device__ __forceinline__ void router_task_j(const Params &p, const float *__re
 
 // Router partial logits ((expert, K chunk) tasks) and the shared expert's gate/up
 // partials, together: both read only the MoE input.
+template <bool NARROW>
 __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
   const int TR = p.E * (p.h / p.pl.kc_router);
   const int Nsh = 2 * p.Is;
@@ -561,8 +576,8 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
       else
         router_task_j<2>(p, w.w_router, u, e, c, cx.lane);
     } else {
-      linear_task<kW8B128>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u, p.M,
-                           p.s.p_sh);
+      linear_task<kW8B128, NARROW ? 1 : 3>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u,
+                                           p.M, p.s.p_sh);
     }
   }
 }
@@ -997,18 +1012,20 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   }
 }
 
-// Routed gate/up tasks (selected expert, 16-row tile of gate and of up), task t to wave t mod waves
+// Routed gate/up tasks (selected expert, 16-row tile of gate and of up), task t to wave t mod waves.
+// NARROW: hidden 4096 and at most 8 rows (one 16-row group).
+template <bool NARROW>
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                   const uint16_t *u, uint8_t *sl) {
   const int tiles_n = p.I >> 4;
   const int T = R.nd * tiles_n;
-  const int qv = p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
+  const int qv = NARROW ? 2 : p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
-    const int ncg = (ce + 15) >> 4;
+    const int ncg = NARROW ? 1 : (ce + 15) >> 4;
     if (qv && ce <= 2) {
-      if (qv == 1) {
+      if (!NARROW && qv == 1) {
         if (ce == 1) routed_gate_up_valu<1, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
         else routed_gate_up_valu<2, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
       } else {
@@ -1025,18 +1042,19 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
 }
 
 // Routed down tasks (expert, tile of TR output rows), task t to wave t mod waves
-template <int TR>
+// NARROW: expert inter other than 4096 and at most 8 rows.
+template <int TR, bool NARROW>
 __device__ __forceinline__ void st_routed_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                                uint8_t *sl) {
   const int tiles_n = p.h / TR;
   const int T = R.nd * tiles_n;
-  const int qv = p.I == 2048 ? 1 : p.I == 4096 ? 2 : 0;  // VALU path: K = 2048 q
+  const int qv = p.I == 2048 ? 1 : !NARROW && p.I == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw; t < T; t += cx.nw) {
     const int q = t / tiles_n, tile = t - q * tiles_n;
     // wave-uniform: keep them (and the addresses built on them) in scalar registers
     const int e = __builtin_amdgcn_readfirstlane(R.list[q]);
     const int ce = __builtin_amdgcn_readfirstlane(R.cnt[e]), p0 = __builtin_amdgcn_readfirstlane(R.start[e]);
-    const int ncg = (ce + 15) >> 4;
+    const int ncg = NARROW ? 1 : (ce + 15) >> 4;
     if (qv == 1 && ce <= 4) {
       if (ce == 1) routed_down_valu<1, 1, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
       else if (ce == 2) routed_down_valu<2, 1, TR>(p, w, e, p0, ce, tile, cx.lane, sl);
@@ -1057,15 +1075,17 @@ __device__ __forceinline__ void st_routed_down(const Params &p, const Ctx &cx, c
 // Shared down partials, then the routed down tasks: tiles of 16 output rows for a few
 // rows (more tasks to spread over the waves), 32 when the step is wide (each task's
 // activation rows are then read once per 32 weight rows).
+template <bool NARROW>
 __device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                         uint8_t *sl) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
   for (int t = cx.gw; t < TS; t += cx.nw)
-    linear_task<kW8B128>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M, p.s.p_shd);
-  if (p.M > 8)
-    st_routed_down<32>(p, cx, w, R, sl);
+    linear_task<kW8B128, NARROW ? 1 : 3>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M,
+                                         p.s.p_shd);
+  if (!NARROW && p.M > 8)
+    st_routed_down<32, NARROW>(p, cx, w, R, sl);
   else
-    st_routed_down<16>(p, cx, w, R, sl);
+    st_routed_down<16, NARROW>(p, cx, w, R, sl);
 }
 
 // m = shared + sum_j w_j y_j in float32 (shared first, slots in emission order);
@@ -1282,6 +1302,12 @@ constexpr unsigned kBarrierThread = kThreads - kWave;
 #define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
   const dsl_kv &kv = A_.kv; const Ctx cx = make_ctx(); (void)p; (void)w; (void)kv; (void)cx
 
+// Two instantiations: the general one, and NARROW for steps of at most 8 rows at the
+// full-size dimensions (hidden 4096, q and o rank 1024, head dim 512, expert inter other
+// than 4096; narrow_dims checks them), which compiles in only the variants those use.  The
+// narrow kernel is about a third of the general one's code, and its fewer spills and
+// instruction-cache misses save about 5 us per launch at 6 rows.
+template <bool NARROW>
 __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   (void)p_arg;
   __shared__ Routing R;
@@ -1327,30 +1353,36 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           cb_base[cx.wave] = cb_read_base(p, cx);
         }
         const uint16_t *xin = A_.xin;
-        switch (row_elems(p.h)) {
-          case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
-          case 2: st_attn_norm_e<2>(p, w, kv, xin, red); break;
-          case 4: st_attn_norm_e<4>(p, w, kv, xin, red); break;
-          case 8: st_attn_norm_e<8>(p, w, kv, xin, red); break;
-          default: st_attn_norm_e<16>(p, w, kv, xin, red); break;
+        if constexpr (NARROW) {
+          st_attn_norm_e<8>(p, w, kv, xin, red);
+        } else {
+          switch (row_elems(p.h)) {
+            case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
+            case 2: st_attn_norm_e<2>(p, w, kv, xin, red); break;
+            case 4: st_attn_norm_e<4>(p, w, kv, xin, red); break;
+            case 8: st_attn_norm_e<8>(p, w, kv, xin, red); break;
+            default: st_attn_norm_e<16>(p, w, kv, xin, red); break;
+          }
         }
       }
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
       {
         STAGE(l);
-        linear_all_pre<kW8T32>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M, p.s.p_qkv, pf_wqkv);
+        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M,
+                                               p.s.p_qkv, pf_wqkv);
       }
       SYNC();
       PreA pf_wq_b = pre_none();
       {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb);
-        st_qkv_post(p, w, kv, red, &wave_lds[0][0]);
+        st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0]);
       }
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
       {
         STAGE(l);
-        linear_all_pre<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M, p.s.p_q, pf_wq_b);
+        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M,
+                                               p.s.p_q, pf_wq_b);
       }
       SYNC();
       PreA pf_wo_a = pre_none();
@@ -1358,11 +1390,15 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa);
         float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
-        switch (p.D) {
-          case 64: st_attention_v<1>(p, cx, kv, lds); break;
-          case 128: st_attention_v<2>(p, cx, kv, lds); break;
-          case 256: st_attention_v<4>(p, cx, kv, lds); break;
-          default: st_attention_v<8>(p, cx, kv, lds); break;
+        if constexpr (NARROW) {
+          st_attention_v<8>(p, cx, kv, lds);
+        } else {
+          switch (p.D) {
+            case 64: st_attention_v<1>(p, cx, kv, lds); break;
+            case 128: st_attention_v<2>(p, cx, kv, lds); break;
+            case 256: st_attention_v<4>(p, cx, kv, lds); break;
+            default: st_attention_v<8>(p, cx, kv, lds); break;
+          }
         }
       }
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
@@ -1375,8 +1411,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
           st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave]);
         } else {
-          linear_all_pre<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M, p.s.p_t,
-                                 pf_wo_a);
+          linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M,
+                                                 p.s.p_t, pf_wo_a);
         }
       }
       if (!fold) {
@@ -1384,12 +1420,16 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         {
           STAGE(l);
           pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
-          switch (row_elems(p.orr)) {
-            case 1: st_t_quant_e<1>(p); break;
-            case 2: st_t_quant_e<2>(p); break;
-            case 4: st_t_quant_e<4>(p); break;
-            case 8: st_t_quant_e<8>(p); break;
-            default: st_t_quant_e<16>(p); break;
+          if constexpr (NARROW) {
+            st_t_quant_e<2>(p);
+          } else {
+            switch (row_elems(p.orr)) {
+              case 1: st_t_quant_e<1>(p); break;
+              case 2: st_t_quant_e<2>(p); break;
+              case 4: st_t_quant_e<4>(p); break;
+              case 8: st_t_quant_e<8>(p); break;
+              default: st_t_quant_e<16>(p); break;
+            }
           }
         }
       }
@@ -1398,18 +1438,23 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         STAGE(l);
         // (this wave's own slot, read in wo_a before the barrier)
         if (fold && cx.lane == 0) tq_base[cx.wave] += 2u * (unsigned)((p.H * p.D) / p.pl.kc_oa);
-        linear_all_pre<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a, pf_wo_b);
+        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a,
+                                               pf_wo_b);
       }
       SYNC();
       {
         STAGE(l);
         const uint16_t *xin = A_.xin;
-        switch (row_elems(p.h)) {
-          case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
-          case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
-          case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
-          case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
-          default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+        if constexpr (NARROW) {
+          st_ffn_norm_e<8>(p, w, xin, last, red);
+        } else {
+          switch (row_elems(p.h)) {
+            case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
+            case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
+            case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
+            case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
+            default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+          }
         }
       }
       if (mode == kModeAttn) {
@@ -1422,12 +1467,12 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       STAGE(l);
       // (a MoE step's first stage: before this block's first arrival)
       if (moe_mode && l == 0 && cx.lane == 0) cb_base[cx.wave] = cb_read_base(p, cx);
-      st_router_shared(p, cx, w, moe_mode ? p.x : p.s.u);
+      st_router_shared<NARROW>(p, cx, w, moe_mode ? p.x : p.s.u);
     }
     SYNC();
     {
       STAGE(l);
-      if (p.M <= kTopkInBlockRows) {
+      if (NARROW || p.M <= kTopkInBlockRows) {
         // no grid barrier between the router and the experts: every block selects the
         // experts of every row itself
         topk_in_block(p, cx, R, moe_mode, last && bid() == 0 ? p.taps.logits : nullptr);
@@ -1452,7 +1497,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     tr.mark();
     {
       STAGE(l);
-      st_routed_gate_up(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
+      st_routed_gate_up<NARROW>(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
       // the shared SwiGLU, off the critical path: its reader, the shared down projection,
       // comes after the next grid barrier
       st_shared_swiglu(p, moe_mode);
@@ -1462,7 +1507,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     {
       STAGE(l);
       cfold = cb_fold(p);
-      st_down(p, cx, w, R, wave_lds[cx.wave]);
+      st_down<NARROW>(p, cx, w, R, wave_lds[cx.wave]);
       if (cfold) cb_count_combine(p, cx, R, moe_mode, last, A_.xout, cb_base);
     }
     if (!cfold) {
@@ -1526,6 +1571,22 @@ static int fail(int code, const char *fmt, ...) {
   } while (0)
 
 static bool mult(int v, int m) { return v > 0 && v % m == 0; }
+
+// Elements per thread of a row of n over the block (the device's row_elems)
+static int row_elems_host(int n) {
+  int e = 1;
+  while (e * kThreads < n) e <<= 1;
+  return e;
+}
+
+// The dimensions and widths the narrow kernel instantiation covers: at most 8 rows (the
+// in-block top-k, 16-column down tiles, one 16-row group of every linear), 8 elements per
+// thread of a hidden row, 2 of a q-rank and of an o-rank row, head dim 512, hidden 4096
+// (the VALU gate/up path for K = 4096) and expert inter other than 4096.
+static bool narrow_dims(const dsl_dims &d, int M) {
+  return M <= 8 && d.hidden == 4096 && row_elems_host(d.q_rank) == 2 && row_elems_host(d.o_rank) == 2 &&
+         d.head_dim == 512 && d.inter != 4096;
+}
 
 static int validate_dims(const dsl_dims *d) {
   if (d->max_rows < 1 || d->max_rows > DSL_MAX_ROWS)
@@ -1650,8 +1711,10 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   HIPCHK(hipGetDeviceProperties(&prop, dev));
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(DSL_EUNSUPPORTED, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
-  int bpc = 0;
-  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel, kThreads, 0));
+  int bpc = 0, bpc_narrow = 0;
+  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel<false>, kThreads, 0));
+  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc_narrow, (const void *)dsl_layer_kernel<true>, kThreads, 0));
+  if (bpc_narrow < bpc) bpc = bpc_narrow;  // one grid for both kernels
   if (bpc < 1) return fail(DSL_EUNSUPPORTED, "the layer kernel cannot be resident on a compute unit");
   if (bpc > 1) bpc = 1;
   dsl_layer *L = new dsl_layer();
@@ -1752,7 +1815,8 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   // A plain launch: one block per compute unit is all that fits (the occupancy check at
   // build), so on a device this launch has to itself every block is resident at once.
   // The cooperative launch path costs ~18 us more per launch on this device.
-  HIPCHK(hipLaunchKernel((const void *)dsl_layer_kernel, dim3(L->grid), dim3(kThreads), args, 0, (hipStream_t)stream));
+  const void *kern = narrow_dims(L->d, M) ? (const void *)dsl_layer_kernel<true> : (const void *)dsl_layer_kernel<false>;
+  HIPCHK(hipLaunchKernel(kern, dim3(L->grid), dim3(kThreads), args, 0, (hipStream_t)stream));
   return 0;
 }
 

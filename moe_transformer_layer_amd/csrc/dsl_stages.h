@@ -405,12 +405,14 @@ __device__ __forceinline__ void linear_task_n(int t, int lane, const uint8_t *W,
   }
 }
 
-template <int FMT>
+// MAXG: the most 16-row groups of x the caller can pass (1: M <= 16, and only that
+// instantiation is compiled in)
+template <int FMT, int MAXG = 3>
 __device__ __forceinline__ void linear_task(int t, int lane, const uint8_t *W, const uint8_t *S8, const float *S32,
                                             int N, int K, int kc, const uint16_t *x, int M, float *part,
                                             const PreA *pf = nullptr, bool use = false) {
   const int ncg = (M + 15) >> 4;
-  if (ncg == 1)
+  if (MAXG == 1 || ncg == 1)
     linear_task_n<FMT, 1>(t, lane, W, S8, S32, N, K, kc, x, M, part, pf, use);
   else if (ncg == 2)
     linear_task_n<FMT, 2>(t, lane, W, S8, S32, N, K, kc, x, M, part, pf, use);
@@ -419,22 +421,22 @@ __device__ __forceinline__ void linear_task(int t, int lane, const uint8_t *W, c
 }
 
 // Task t of a dense linear to global wave t mod waves.
-template <int FMT>
+template <int FMT, int MAXG = 3>
 __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N, int K, int kc,
                            const uint16_t *x, int M, float *part) {
   const int T = (N >> 4) * (K / kc);
-  for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+  for (int t = cx.gw; t < T; t += cx.nw) linear_task<FMT, MAXG>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
 }
 
 // The same, the wave's first task starting from the weights linear_prefetch loaded.
-template <int FMT>
+template <int FMT, int MAXG = 3>
 __device__ __forceinline__ void linear_all_pre(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N,
                                                int K, int kc, const uint16_t *x, int M, float *part, const PreA &pf) {
   const int T = (N >> 4) * (K / kc);
   int t = cx.gw;
-  if (t < T) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part, &pf, pf.on);
+  if (t < T) linear_task<FMT, MAXG>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part, &pf, pf.on);
   // (the first task peeled: pf is dead after it)
-  for (t += cx.nw; t < T; t += cx.nw) linear_task<FMT>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
+  for (t += cx.nw; t < T; t += cx.nw) linear_task<FMT, MAXG>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
 }
 
 // Where this wave's first task of linear_all_pre (same arguments) starts, when it has
