@@ -1406,7 +1406,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       bool fold;
       {
         STAGE(l);
-        fold = tq_fold(p);
+        fold = NARROW || tq_fold(p);  // (the host picks the narrow kernel only where it holds)
         if (fold) {
           pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
           st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave]);
@@ -1506,7 +1506,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     bool cfold;
     {
       STAGE(l);
-      cfold = cb_fold(p);
+      cfold = NARROW || cb_fold(p);  // (likewise)
       st_down<NARROW>(p, cx, w, R, wave_lds[cx.wave]);
       if (cfold) cb_count_combine(p, cx, R, moe_mode, last, A_.xout, cb_base);
     }
@@ -1586,6 +1586,19 @@ static int row_elems_host(int n) {
 static bool narrow_dims(const dsl_dims &d, int M) {
   return M <= 8 && d.hidden == 4096 && row_elems_host(d.q_rank) == 2 && row_elems_host(d.o_rank) == 2 &&
          d.head_dim == 512 && d.inter != 4096;
+}
+
+// The narrow kernel also assumes that both folds apply (it has no t_quant or combine
+// stage): the conditions of tq_fold and cb_fold for this launch's grid and buffers.
+static bool narrow_ok(const dsl_layer *L, const Params &p) {
+  if (!narrow_dims(L->d, p.M)) return false;
+  const int nw = L->grid * kWavesPerBlock;
+  const int T_oa = (p.orr >> 4) * ((p.H * p.D) / p.pl.kc_oa);
+  const bool tq = p.M <= 16 && T_oa <= nw && p.orr / 32 <= kTqGroups;
+  const int ntile = p.h >> 4;
+  const bool al = ((uintptr_t)p.out & 3u) == 0 && ((uintptr_t)p.taps.moe_out & 3u) == 0;
+  const bool cb = p.M <= 8 && (p.h & 31) == 0 && ntile > 0 && nw % ntile == 0 && (p.h >> 5) <= kCbGroups && al;
+  return tq && cb;
 }
 
 static int validate_dims(const dsl_dims *d) {
@@ -1815,7 +1828,7 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   // A plain launch: one block per compute unit is all that fits (the occupancy check at
   // build), so on a device this launch has to itself every block is resident at once.
   // The cooperative launch path costs ~18 us more per launch on this device.
-  const void *kern = narrow_dims(L->d, M) ? (const void *)dsl_layer_kernel<true> : (const void *)dsl_layer_kernel<false>;
+  const void *kern = narrow_ok(L, p) ? (const void *)dsl_layer_kernel<true> : (const void *)dsl_layer_kernel<false>;
   HIPCHK(hipLaunchKernel(kern, dim3(L->grid), dim3(kThreads), args, 0, (hipStream_t)stream));
   return 0;
 }
