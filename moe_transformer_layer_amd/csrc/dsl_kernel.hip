@@ -1304,9 +1304,10 @@ constexpr unsigned kBarrierThread = kThreads - kWave;
 
 // Two instantiations: the general one, and NARROW for steps of at most 8 rows at the
 // full-size dimensions (hidden 4096, q and o rank 1024, head dim 512, expert inter other
-// than 4096; narrow_dims checks them), which compiles in only the variants those use.  The
-// narrow kernel is about a third of the general one's code with half the spills, and
-// takes about 4 us less per launch at 6 rows.
+// than 4096), which compiles in only the variants those use and, since the t_quant and
+// combine folds always apply there, neither of the stages they replace (narrow_ok checks
+// all of it on the host).  The narrow kernel is under a third of the general one's code
+// with under half the spills, and takes about 6 us less per launch at 6 rows.
 template <bool NARROW>
 __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   (void)p_arg;
