@@ -568,7 +568,8 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
   const int Nsh = 2 * p.Is;
   const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
   const int J = (p.pl.kc_router + 511) >> 9;
-  for (int t = cx.gw; t < TR + TS; t += cx.nw) {
+  // (narrow: at most one task per wave, which the host checks)
+  for (int t = cx.gw; t < TR + TS; t += NARROW ? 1 << 30 : cx.nw) {
     if (t < TR) {
       const int e = t % p.E, c = t / p.E;
       if (J == 1)
@@ -1079,7 +1080,7 @@ template <bool NARROW>
 __device__ __forceinline__ void st_down(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                         uint8_t *sl) {
   const int TS = (p.h >> 4) * (p.Is / p.pl.kc_shd);
-  for (int t = cx.gw; t < TS; t += cx.nw)
+  for (int t = cx.gw; t < TS; t += NARROW ? 1 << 30 : cx.nw)  // (narrow: at most one task per wave)
     linear_task<kW8B128, NARROW ? 1 : 3>(t, cx.lane, w.sh_wd, nullptr, w.sh_wd_s, p.h, p.Is, p.pl.kc_shd, p.s.zsh, p.M,
                                          p.s.p_shd);
   if (!NARROW && p.M > 8)
@@ -1369,7 +1370,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
       {
         STAGE(l);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M,
+        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M,
                                                p.s.p_qkv, pf_wqkv);
       }
       SYNC();
@@ -1382,7 +1383,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
       {
         STAGE(l);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M,
+        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M,
                                                p.s.p_q, pf_wq_b);
       }
       SYNC();
@@ -1412,7 +1413,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
           st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave]);
         } else {
-          linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M,
+          linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M,
                                                  p.s.p_t, pf_wo_a);
         }
       }
@@ -1439,7 +1440,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         STAGE(l);
         // (this wave's own slot, read in wo_a before the barrier)
         if (fold && cx.lane == 0) tq_base[cx.wave] += 2u * (unsigned)((p.H * p.D) / p.pl.kc_oa);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a,
+        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a,
                                                pf_wo_b);
       }
       SYNC();
@@ -1594,6 +1595,14 @@ static bool narrow_dims(const dsl_dims &d, int M) {
 static bool narrow_ok(const dsl_layer *L, const Params &p) {
   if (!narrow_dims(L->d, p.M)) return false;
   const int nw = L->grid * kWavesPerBlock;
+  // at most one task per wave in the dense linears, the router and shared gate/up stage and
+  // the shared down (the narrow kernel compiles in only a wave's first task of each)
+  const int T[] = {((p.qr + p.D) >> 4) * (p.h / p.pl.kc_qkv), ((p.H * p.D) >> 4) * (p.qr / p.pl.kc_qb),
+                   (p.orr >> 4) * ((p.H * p.D) / p.pl.kc_oa), (p.h >> 4) * (p.orr / p.pl.kc_ob),
+                   p.E * (p.h / p.pl.kc_router) + ((2 * p.Is) >> 4) * (p.h / p.pl.kc_sh13),
+                   (p.h >> 4) * (p.Is / p.pl.kc_shd)};
+  for (int t : T)
+    if (t > nw) return false;
   const int T_oa = (p.orr >> 4) * ((p.H * p.D) / p.pl.kc_oa);
   const bool tq = p.M <= 16 && T_oa <= nw && p.orr / 32 <= kTqGroups;
   const int ntile = p.h >> 4;

@@ -429,12 +429,14 @@ __device__ __forceinline__ void linear_all(const Ctx &cx, const uint8_t *W, cons
 }
 
 // The same, the wave's first task starting from the weights linear_prefetch loaded.
-template <int FMT, int MAXG = 3>
+// ONE: the caller knows there are no more tasks than waves (only the first task is compiled).
+template <int FMT, int MAXG = 3, bool ONE = false>
 __device__ __forceinline__ void linear_all_pre(const Ctx &cx, const uint8_t *W, const uint8_t *S8, const float *S32, int N,
                                                int K, int kc, const uint16_t *x, int M, float *part, const PreA &pf) {
   const int T = (N >> 4) * (K / kc);
   int t = cx.gw;
   if (t < T) linear_task<FMT, MAXG>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part, &pf, pf.on);
+  if constexpr (ONE) return;
   // (the first task peeled: pf is dead after it)
   for (t += cx.nw; t < T; t += cx.nw) linear_task<FMT, MAXG>(t, cx.lane, W, S8, S32, N, K, kc, x, M, part);
 }
