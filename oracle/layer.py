@@ -273,14 +273,17 @@ def layer_step(d, lw: dict, x_bits: np.ndarray, kv, cache: np.ndarray) -> dict:
                 attn=at, moe=mo)
 
 
-def decode_step(d, layers: list, x_bits: np.ndarray, kv, caches: list) -> dict:
+def decode_step(d, layers: list, x_bits: np.ndarray, kv, caches: list, on_layer=None) -> dict:
     """n_layers chained layers (the draft model runs three): layer l's output is layer
     l+1's input; each layer has its own weights and its own cache, the tables are
     shared.  `caches` are updated in place (pass copies).  Returns the last layer's
-    outputs and every layer's results."""
+    outputs and every layer's results.  `on_layer(l)`, when given, is called before
+    layer l starts (progress reporting only)."""
     per = []
     x = x_bits
     for l in range(d.n_layers):
+        if on_layer is not None:
+            on_layer(l)
         r = layer_step(d, layers[l], x, kv, caches[l])
         per.append(r)
         x = r["out"]

@@ -181,9 +181,9 @@ def min_gap(d, res_layers: list, live) -> float:
     return g
 
 
-def oracle_decode(case):
+def oracle_decode(case, on_layer=None):
     caches = [c.copy() for c in case.kv.cache]
-    res = OL.decode_step(case.dims, case.layers, case.x, case.kv, caches)
+    res = OL.decode_step(case.dims, case.layers, case.x, case.kv, caches, on_layer=on_layer)
     return res, caches
 
 

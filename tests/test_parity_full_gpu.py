@@ -126,7 +126,7 @@ def _case_and_oracle(dsl, name, key):
     layout = {k: sd[k] for k in ("M", "n_req", "rows_per_req", "n_pad") if k in sd}
     case = synth.make_case(name, sd["seed"], layers=layers, **layout)
     _say(f"{key}: oracle, {case.dims.n_layers} layer(s) at M={case.M}")
-    res, caches = oracle_decode(case)
+    res, caches = oracle_decode(case, on_layer=lambda l: _say(f"{key}: oracle layer {l}"))
     live = decode_live(case)
     g = min_gap(case.dims, res["layers"], live)
     assert g >= GAP_MIN, f"{key}: top-k gap {g} below {GAP_MIN}"
@@ -264,6 +264,7 @@ def test_attention_half_m48(dsl):
     _say(f"attn48: ok {rep}")
 
 
+@pytest.mark.timeout(300)
 def test_full_layer_m48_top6(dsl):
     _run_decode(dsl, "layer48", "layer48_m48")
 
@@ -272,6 +273,9 @@ def test_full_layer_m6_top6(dsl):
     _run_decode(dsl, "layer48", "layer48_m6")
 
 
+# The CPU oracle of three chained layers takes about two minutes at M=48 on the GPU
+# host's cores; the limit leaves room for a slower host.
+@pytest.mark.timeout(480)
 @pytest.mark.parametrize("M", [1, 6, 12, 16, 17, 24, 36, 48])
 def test_draft_three_layers(dsl, M):
     _run_chain(dsl, "draft", f"draft_m{M}")
