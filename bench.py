@@ -5,6 +5,9 @@ attention back, MoE) over one batch of rows, launched through the C ABI as one
 persistent kernel.  Weights are cold: the bench holds L distinct copies of the
 layer's weights in HBM (as a model holds distinct layers) and step i runs copy
 i mod L, so no step finds the previous one's weights in the 256 MB Infinity Cache.
+Step i also reads input i mod P of a pool of P seeded draws, so the selected experts
+and their load change from step to step; each step's algorithmic bytes are counted
+from its own expert ids.
 
 Prints one JSON line: the M=6 full layer (top-6 of 128 experts) as the headline,
 the M=48 layer and the three chained draft layers at M=6 (top-3, per layer) as
@@ -62,11 +65,15 @@ def algorithmic_bytes(d, M: int, layer_ids, kv) -> dict:
 
 
 def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup: int, weights, seed: int = 0,
-              graph_replay: bool = True):
+              graph_replay: bool = True, pool: int = 16):
     """Times `steps` launches of workload `name` at M rows, rotating over `layers_dev`
-    device copies of the weights: once for the wall time, once more with HIP events on
-    the launch stream around every launch for the kernel time; then replays the same
-    launches from a captured HIP graph for the launch-gap-free wall time."""
+    device copies of the weights and over a pool of `pool` input draws (so the selected
+    experts and their load change from launch to launch): once for the wall time, once
+    more with HIP events on the launch stream around every launch for the kernel time;
+    then replays the same launches from a captured HIP graph for the launch-gap-free wall
+    time.  The algorithmic bytes of each launch come from its own input's expert ids."""
+    import numpy as np
+
     from moe_transformer_layer_amd import synth
     case = synth.make_case(name, seed, M=M, layers=weights)
     d = case.dims
@@ -79,21 +86,26 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
         copies.append(wd)
         ws = [dsl.Weights(**{k: lw[k].data_ptr() for k in dsl.WEIGHT_FIELDS}) for lw in wd]
         handles.append(dsl.dsl_layer_build(dsl.dims_struct(d), ws))
-    x = torch.from_numpy(case.x.view("int16")).to(dev.dev)
-    out = torch.zeros_like(x)
+    rng = np.random.default_rng([seed, 99])
+    xs_h = [case.x] + [synth.gen_x(d, rng, M) for _ in range(pool - 1)]
+    xs = [torch.from_numpy(x.view("int16")).to(dev.dev) for x in xs_h]
+    out = torch.zeros_like(xs[0])
     layer_ids = torch.zeros((d.n_layers, M, d.top_k), dtype=torch.int32, device=dev.dev)
     taps = dsl.Taps(None, None, None, None, None, None, None, layer_ids.data_ptr())
     stream = dev.stream()
     for hnd in handles:
         dsl.dsl_layer_reserve(hnd, M)
-    dsl.dsl_decode_step(handles[0], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(), out.data_ptr(),
-                        taps, stream)
-    torch.cuda.synchronize()
-    ids_h = layer_ids.cpu().numpy()
+    # every pool entry's expert ids (the weight copies are identical, so any handle gives them)
+    byts = []
+    for x in xs:
+        dsl.dsl_decode_step(handles[0], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(), out.data_ptr(),
+                            taps, stream)
+        torch.cuda.synchronize()
+        byts.append(algorithmic_bytes(d, M, layer_ids.cpu().numpy(), case.kv))
 
     def step(i, strm):
-        dsl.dsl_decode_step(handles[i % len(handles)], x.data_ptr(), M, dev.kv_structs, dev.positions.data_ptr(),
-                            out.data_ptr(), None, strm)
+        dsl.dsl_decode_step(handles[i % len(handles)], xs[i % pool].data_ptr(), M, dev.kv_structs,
+                            dev.positions.data_ptr(), out.data_ptr(), None, strm)
 
     for i in range(warmup):
         step(i, stream)
@@ -135,10 +147,19 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
         rc = dsl.dsl_layer_health(hnd)
         if rc:
             raise RuntimeError(f"device fault reported: {dsl.dsl_last_error()}")
-    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # microseconds per launch
+    times = [a.elapsed_time(b) * 1e3 for a, b in ev]  # microseconds per launch
+    per = sorted(times)
     mean_us = sum(per) / len(per)
-    byts = algorithmic_bytes(d, M, ids_h, case.kv)
-    gbs = byts["total"] / (mean_us * 1e-6) / 1e9
+    # the timed launches' own algorithmic bytes: launch i read input i mod pool
+    launch_bytes = [byts[i % pool]["total"] for i in range(steps)]
+    mean_bytes = sum(launch_bytes) / steps
+    gbs = mean_bytes / (mean_us * 1e-6) / 1e9
+    nd = [sum(byts[i % pool]["n_distinct"]) / d.n_layers for i in range(steps)]
+    bsum = dict(byts[0])
+    bsum.update(total=mean_bytes, per_layer=mean_bytes / d.n_layers, experts=None,
+                n_distinct=None, n_distinct_per_layer={"min": min(nd), "mean": sum(nd) / len(nd), "max": max(nd)},
+                total_min=min(launch_bytes), total_max=max(launch_bytes), pool=pool,
+                kind="mean over the timed launches of each launch's own algorithmic bytes")
     for hnd in handles[1:]:
         dsl.dsl_layer_destroy(hnd)
     grid = dsl.dsl_layer_grid(dev.handle)
@@ -152,7 +173,7 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
                 us_kernel_mean=mean_us,
                 us_per_layer_kernel=mean_us / nl, us_kernel_p10=per[len(per) // 10],
                 us_kernel_p50=per[len(per) // 2], us_kernel_p90=per[(9 * len(per)) // 10], gbs=gbs,
-                frac=gbs / PEAK_GBS, bytes=byts, grid=grid, n_weight_copies=len(handles))
+                frac=gbs / PEAK_GBS, bytes=bsum, grid=grid, n_weight_copies=len(handles))
 
 
 def copy_gbs(torch, mib: int = 1024, reps: int = 10) -> float:
@@ -342,7 +363,7 @@ def main():
                                "cold weights", "rows": 6, "seq_context": "1k-64k paged, block 128"},
         "roofline": {"bound": "hbm", "achieved": round(m6["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(m6["frac"], 4), "traffic": measured_traffic(),
-                     "algorithmic_bytes": m6["bytes"]["total"], "kernel_us_mean": round(m6["us_kernel_mean"], 2),
+                     "algorithmic_bytes": round(m6["bytes"]["total"]), "kernel_us_mean": round(m6["us_kernel_mean"], 2),
                      "copy_gbs": round(copy, 1), "frac_of_copy": round(m6["gbs"] / copy, 4)},
         "m6": m6,
         "m48": m48,

@@ -191,6 +191,12 @@ int dsl_layer_health(dsl_layer *layer);
 int dsl_layer_set_trace(dsl_layer *layer, int32_t on);
 int dsl_layer_read_trace(dsl_layer *layer, double *ns, int32_t n_marks);
 
+/* Which instantiation of the layer kernel the handle's most recent step launched: 1 =
+ * the narrow one (steps of at most 8 rows at hidden 4096, q/o rank 1024, head dim 512),
+ * 0 = the general one, -1 = no step yet (DSL_EINVAL for a NULL handle).  For tests and
+ * reports: the results do not depend on it. */
+int dsl_layer_last_kernel(const dsl_layer *layer);
+
 /* Grid the persistent launch uses (blocks, threads per block); for reports. */
 int dsl_layer_grid(const dsl_layer *layer, int32_t *blocks, int32_t *threads);
 

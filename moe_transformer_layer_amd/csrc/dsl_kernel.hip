@@ -1559,6 +1559,7 @@ struct WidthScratch {
 struct dsl_layer {
   dsl_dims d{};
   int dev = 0, cus = 0, grid = 0, bpc = 0, S = 1;
+  int last_kernel = -1;  // instantiation of the most recent launch: 1 narrow, 0 general
   Plan plan{};
   dsl_weights *dw = nullptr;  // device copy of the weight descriptors
   SyncWords *sync = nullptr;
@@ -1852,8 +1853,10 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   // A plain launch: one block per compute unit is all that fits (the occupancy check at
   // build), so on a device this launch has to itself every block is resident at once.
   // The cooperative launch path costs ~18 us more per launch on this device.
-  const void *kern = narrow_ok(L, p) ? (const void *)dsl_layer_kernel<true> : (const void *)dsl_layer_kernel<false>;
+  const bool narrow = narrow_ok(L, p);
+  const void *kern = narrow ? (const void *)dsl_layer_kernel<true> : (const void *)dsl_layer_kernel<false>;
   HIPCHK(hipLaunchKernel(kern, dim3(L->grid), dim3(kThreads), args, 0, (hipStream_t)stream));
+  L->last_kernel = narrow ? 1 : 0;
   return 0;
 }
 
@@ -1923,6 +1926,11 @@ int dsl_layer_read_trace(dsl_layer *L, double *ns, int32_t n_marks) {
       ns[(size_t)i * G + b] = v ? ((double)v - (double)t0) * 1e6 / khz : -1.0;
     }
   return cnt < n_marks ? cnt : n_marks;
+}
+
+int dsl_layer_last_kernel(const dsl_layer *L) {
+  if (!L) return fail(DSL_EINVAL, "layer is NULL");
+  return L->last_kernel;
 }
 
 int dsl_layer_grid(const dsl_layer *L, int32_t *blocks, int32_t *threads) {

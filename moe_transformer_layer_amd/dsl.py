@@ -73,13 +73,15 @@ def lib() -> ctypes.CDLL:
         L.dsl_moe_step.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
         L.dsl_layer_health.argtypes = [c_void_p]
         L.dsl_layer_grid.argtypes = [c_void_p, P(c_int32), P(c_int32)]
+        L.dsl_layer_last_kernel.argtypes = [c_void_p]
         L.dsl_layer_set_trace.argtypes = [c_void_p, c_int32]
         L.dsl_layer_read_trace.argtypes = [c_void_p, ctypes.POINTER(ctypes.c_double), c_int32]
         L.dsl_layer_destroy.argtypes = [c_void_p]
         L.dsl_layer_destroy.restype = None
         L.dsl_last_error.restype = ctypes.c_char_p
         for f in ("dsl_layer_build", "dsl_layer_reserve", "dsl_decode_step", "dsl_attn_step", "dsl_moe_step",
-                  "dsl_layer_health", "dsl_layer_grid", "dsl_layer_set_trace", "dsl_layer_read_trace"):
+                  "dsl_layer_health", "dsl_layer_grid", "dsl_layer_set_trace", "dsl_layer_read_trace",
+                  "dsl_layer_last_kernel"):
             getattr(L, f).restype = c_int32
         _lib = L
     return _lib
@@ -132,6 +134,15 @@ def dsl_layer_grid(h) -> tuple:
     b, t = c_int32(), c_int32()
     _check(lib().dsl_layer_grid(h, ctypes.byref(b), ctypes.byref(t)))
     return b.value, t.value
+
+
+def dsl_layer_last_kernel(h) -> int:
+    """1 if the handle's most recent step ran the narrow kernel instantiation, 0 if the
+    general one, -1 before any step."""
+    rc = lib().dsl_layer_last_kernel(h)
+    if rc < -1:
+        _check(rc)
+    return rc
 
 
 def dsl_layer_set_trace(h, on: bool):

@@ -31,7 +31,21 @@ CASES = {
     # either side of 16 rows (2 requests x (1 + 7 drafts), and one pad row more)
     "draft_m16": ("draft", 11, dict(n_req=2, rows_per_req=8), "decode"),
     "draft_m17": ("draft", 11, dict(n_req=2, rows_per_req=8, n_pad=1), "decode"),
+    # steps of at most 8 rows at the full size, with and without a pad row
+    "layer48_m2": ("layer48", 7, dict(n_req=1, rows_per_req=2), "decode"),
+    "layer48_m8": ("layer48", 7, dict(n_req=1, rows_per_req=8), "decode"),
+    "layer48_m6p1": ("layer48", 7, dict(n_req=1, rows_per_req=5, n_pad=1), "decode"),
+    "layer48_m8p1": ("layer48", 7, dict(n_req=1, rows_per_req=7, n_pad=1), "decode"),
+    "draft_m6p1": ("draft", 11, dict(n_req=1, rows_per_req=5, n_pad=1), "decode"),
+    # the graph replay stress: both of its input sets (the case's x, and a second draw)
+    "stress_m48": ("layer48", 5, dict(M=48), "stress"),
+    "stress_m6": ("layer48", 5, dict(M=6), "stress"),
 }
+
+
+def second_input(case):
+    """The stress test's second input set for a case: a fresh draw of the same shape."""
+    return synth.gen_x(case.dims, np.random.default_rng([case.seed, 77]), case.M)
 
 
 def gap_of(case, kind):
@@ -39,11 +53,16 @@ def gap_of(case, kind):
     if kind == "moe":
         r = OL.moe_step(d, case.layers[0], case.x)
         return float(OL.topk_gap(r["logits"], d.top_k).min()), [r["n_distinct"]]
-    caches = [c.copy() for c in case.kv.cache]
-    r = OL.decode_step(d, case.layers, case.x, case.kv, caches)
     live = case.kv.positions >= 0
-    g = min(float(OL.topk_gap(x["logits"], d.top_k)[live].min()) for x in r["layers"])
-    return g, [x["n_distinct"] for x in r["layers"]]
+    g, nd = np.inf, []
+    for x in ([case.x, second_input(case)] if kind == "stress" else [case.x]):
+        caches = [c.copy() for c in case.kv.cache]
+        r = OL.decode_step(d, case.layers, x, case.kv, caches)
+        g = min(g, min(float(OL.topk_gap(y["logits"], d.top_k)[live].min()) for y in r["layers"]))
+        nd += [y["n_distinct"] for y in r["layers"]]
+        if g < GAP_MIN:
+            break
+    return g, nd
 
 
 def main(keys):
@@ -63,8 +82,20 @@ def main(keys):
             if g >= GAP_MIN:
                 seeds[key] = dict(config=name, weights_seed=wseed, seed=s, min_gap=g, n_distinct=nd, **kw)
                 break
+        _store(key, seeds.get(key))
+
+
+def _store(key, entry):
+    """Merge one key into seeds.json under a lock (several keys may be searched at once)."""
+    import fcntl
+    if entry is None:
+        return
+    with open(OUT + ".lock", "w") as lk:
+        fcntl.flock(lk, fcntl.LOCK_EX)
+        cur = json.load(open(OUT)) if os.path.exists(OUT) else {}
+        cur[key] = entry
         with open(OUT, "w") as f:
-            json.dump(seeds, f, indent=1, sort_keys=True)
+            json.dump(cur, f, indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":

@@ -173,6 +173,44 @@ def check_records(d, got_cache, want_cache, before, report: dict | None = None):
         assert dv_ratio <= 1.0, f"KV record values differ by up to {dv_ratio:.3g} of their bar"
 
 
+MOE_IN_ULPS = 2
+
+
+class Errors:
+    """Collects the failures of several checks, so that one report lists all of them."""
+
+    def __init__(self):
+        self.msgs, self.rep = [], {}
+
+    def attempt(self, f, *a, rep=None, **kw):
+        try:
+            return f(*a, self.rep if rep is None else rep, **kw)
+        except AssertionError as e:
+            self.msgs.append(str(e))
+
+    def raise_any(self, key, say=print):
+        say(f"{key}: {self.rep}")
+        assert not self.msgs, f"{key}: " + " | ".join(self.msgs)
+
+
+def check_layer(er: Errors, d, lw, got, want, live, got_cache, want_cache, before, tag="L0"):
+    """The per-layer bars of a full decode step: every bf16 output; moe_in within
+    MOE_IN_ULPS bf16 steps (a one-step flip of hres, scaled by gamma / rms in the FFN
+    norm, can round to two steps); logits explained by moe_in's deviation; ids as sets
+    and weights within half the selected logits' deviation; KV records."""
+    rep = er.rep.setdefault(tag, {})
+    for k in ("attn_out", "hres", "moe_out", "out"):
+        er.attempt(check_bf16, f"{tag}.{k}", got[k], want[k], rep=rep)
+    er.attempt(check_bf16, f"{tag}.moe_in", got["moe_in"], want["moe_in"], rep=rep, ulps=MOE_IN_ULPS)
+    dl = er.attempt(check_logits, got["logits"], want["logits"], got["moe_in"], want["moe_in"], lw["w_router"],
+                    live, rep=rep)
+    if dl is not None:
+        sel = np.take_along_axis(np.abs(got["logits"].astype(np.float64) - want["logits"]),
+                                 np.maximum(want["ids"], 0), axis=1).max(axis=1)
+        er.attempt(check_routing, got["ids"], got["w"], want["ids"], want["w"], live, sel / 2 + 1e-6, rep=rep)
+    er.attempt(check_records, d, got_cache, want_cache, before, rep=rep)
+
+
 def min_gap(d, res_layers: list, live) -> float:
     g = np.inf
     for r in res_layers:
@@ -212,5 +250,5 @@ def decode_live(case):
     return case.kv.positions >= 0
 
 
-__all__ = ["synth", "check_bf16", "check_routing", "check_logits", "bf16_ulp", "check_records", "gap_seed", "oracle_decode", "cos",
+__all__ = ["synth", "Errors", "check_layer", "MOE_IN_ULPS", "check_bf16", "check_routing", "check_logits", "bf16_ulp", "check_records", "gap_seed", "oracle_decode", "cos",
            "decode_live", "min_gap", "ATOL", "COS_MIN", "GAP_MIN"]

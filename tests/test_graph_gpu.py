@@ -17,7 +17,10 @@ the eager launch on the same inputs bit for bit, and at the end the caches must 
 the eager launches wrote.
 
   full-size layer (hidden 4096, top-6 of 128), widths 48 and 6:
-      a graph of 50 (48, 6) pairs replayed 1000 times = 100,000 launches
+      a graph of 50 (48, 6) pairs replayed 1000 times = 100,000 launches; the eager
+      launches they are compared with are themselves checked against the oracle first,
+      at the per-layer parity bars, on both input sets (seeds from tests/golden/seeds.json
+      whose top-k gap holds on both)
   two chained draft layers (index-table mode) at small dims, widths 13 and 5:
       a graph of 8 pairs replayed 40 times
 """
@@ -25,6 +28,7 @@ import numpy as np
 import pytest
 
 from moe_transformer_layer_amd import synth
+from parity import Errors, GAP_MIN, check_layer, load_seeds, min_gap
 
 pytestmark = [pytest.mark.gpu]
 
@@ -49,6 +53,7 @@ class _Side:
     def __init__(self, dsl, torch, name, layers, weights, layout, seed, pairs):
         self.dsl, self.torch = dsl, torch
         case = synth.make_case(name, seed, layers=layers, **layout)
+        self.case = case
         d = case.dims
         self.M = M = case.M
         self.dev = dsl.LayerOnDevice(case, weights=weights)
@@ -89,24 +94,59 @@ class _Side:
         return bad
 
 
-def _stress(dsl, name, layouts, pairs, replays, wseed=5):
-    """layouts: one make_case row layout per width (requests x rows per request + pad rows)."""
+def _oracle_check(dsl, side, layers, caches_after):
+    """The eager launches the replays are compared with, against the oracle on the same
+    inputs, at the per-layer parity bars (one-layer cases): input set i's outputs and the
+    cache as that launch left it."""
+    from oracle import layer as OL
+    case = side.case
+    d = case.dims
+    live = case.kv.positions >= 0
+    er = Errors()
+    for i in range(2):
+        x = side.inputs[i].cpu().numpy().view(np.uint16)
+        caches = [c.copy() for c in case.kv.cache]
+        _say(f"oracle: width {side.M}, input set {i}")
+        want = OL.decode_step(d, layers, x, case.kv, caches)
+        g = min_gap(d, want["layers"], live)
+        assert g >= GAP_MIN, f"width {side.M} input set {i}: top-k gap {g} below {GAP_MIN}"
+        ref = {k: v.cpu().numpy() for k, v in side.ref[i].items()}
+        got = dict(ref)
+        for k in ("out", "attn_out", "hres", "moe_in", "moe_out"):
+            got[k] = ref[k].view(np.uint16)
+        got["w"] = ref["w"].view(np.float32)
+        got["logits"] = ref["logits"].view(np.float32)
+        check_layer(er, d, layers[0], got, want, live, caches_after[i][0].cpu().numpy(), caches[0],
+                    case.kv.cache[0], tag=f"M{side.M}.set{i}")
+    er.raise_any(f"eager reference, width {side.M}", _say)
+
+
+def _stress(dsl, name, layouts, pairs, replays, wseed=5, seeds=None, oracle=False):
+    """layouts: one make_case row layout per width (requests x rows per request + pad rows).
+    seeds: each width's input seed (default 100, 101, ...).  oracle: check the eager
+    launches against the oracle first (one-layer workloads)."""
     import torch
     layers = synth.make_weights(name, wseed)
     weights = dsl.DeviceWeights(synth.CONFIGS[name], layers)
-    sides = [_Side(dsl, torch, name, layers, weights, lay, 100 + j, pairs) for j, lay in enumerate(layouts)]
+    seeds = seeds or [100 + j for j in range(len(layouts))]
+    sides = [_Side(dsl, torch, name, layers, weights, lay, seeds[j], pairs) for j, lay in enumerate(layouts)]
     widths = tuple(s.M for s in sides)
     # eager runs: each width once per input set (the first call allocates the width's scratch)
+    caches_after = [[] for _ in sides]
     for i in range(2):
-        for s in sides:
+        for j, s in enumerate(sides):
             s.select(i)
             bufs = {k: torch.full(shp, SENTINEL, dtype=dt, device="cuda") if dt == torch.int32
                     else torch.full(shp, -1, dtype=dt, device="cuda") for k, (shp, dt) in s.shapes.items()}
             s.launch(bufs)
             s.ref.append(bufs)
-    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            caches_after[j].append([c.clone() for c in s.dev.caches])
     dsl._check(dsl.dsl_layer_health(weights.handle))
-    caches_ref = [[c.clone() for c in s.dev.caches] for s in sides]  # after input set 1
+    caches_ref = [c[1] for c in caches_after]  # after input set 1
+    if oracle:
+        for j, s in enumerate(sides):
+            _oracle_check(dsl, s, layers, caches_after[j])
     for s in sides:
         assert not torch.equal(s.ref[0]["out"], s.ref[1]["out"])
         for i in range(2):
@@ -157,6 +197,9 @@ def test_graph_draft_small(dsl):
             pairs=8, replays=40)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_graph_race_stress_full(dsl):
-    _stress(dsl, "layer48", (dict(M=48), dict(M=6)), pairs=50, replays=1000)
+    sd = load_seeds()
+    seeds = [sd[k]["seed"] for k in ("stress_m48", "stress_m6")]
+    assert all(sd[k]["weights_seed"] == 5 for k in ("stress_m48", "stress_m6"))
+    _stress(dsl, "layer48", (dict(M=48), dict(M=6)), pairs=50, replays=1000, seeds=seeds, oracle=True)

@@ -6,10 +6,12 @@ make_seeds.py with the oracle alone); each test re-checks the top-k gap rule.
   MoE stage alone, M = 6, top-3                 (moe6)
   attention half alone, M = 48 (8 x 6 rows)     (attn48)
   full layer, top-6, M = 48 and M = 6           (layer48)
+  full layer at the narrow kernel's widths: 2, 8, 5 + a pad row, 7 + a pad row
+  attention half alone, M = 6 with a pad row
   three draft layers, 192-wide index rows, top-3, M in {1, 6, 12, 16, 17, 24, 36, 48}
   (16 = 2 requests x 8 rows, 17 the same and a pad row: either side of the widest step
-  whose wo_a output quantization is folded into wo_a), one handle for all widths (each
-  width gets its own scratch)  (draft)
+  whose wo_a output quantization is folded into wo_a), and 5 rows + a pad row; one handle
+  for all widths (each width gets its own scratch)  (draft)
 
 Tolerances beyond the common bf16 bar, and why:
 
@@ -47,13 +49,12 @@ import pytest
 from moe_transformer_layer_amd import synth
 from oracle import layer as OL
 from oracle.formats import bf16_value
-from parity import (ATOL, COS_MIN, GAP_MIN, check_bf16, check_logits, check_records, check_routing, cos,
-                    decode_live, load_seeds, min_gap, oracle_decode)
+from parity import (ATOL, COS_MIN, GAP_MIN, Errors, check_bf16, check_layer, check_logits, check_records,
+                    check_routing, cos, decode_live, load_seeds, min_gap, oracle_decode)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 W_TOL_MOE = 1e-5
-MOE_IN_ULPS = 2
 G_DRIFT = 1e-2
 SEEDS = load_seeds()
 
@@ -91,35 +92,6 @@ def _seeded(key):
     return SEEDS[key]
 
 
-class Errors:
-    def __init__(self):
-        self.msgs, self.rep = [], {}
-
-    def attempt(self, f, *a, rep=None, **kw):
-        try:
-            return f(*a, self.rep if rep is None else rep, **kw)
-        except AssertionError as e:
-            self.msgs.append(str(e))
-
-    def raise_any(self, key):
-        _say(f"{key}: {self.rep}")
-        assert not self.msgs, f"{key}: " + " | ".join(self.msgs)
-
-
-def _check_layer(er: Errors, d, lw, got, want, live, got_cache, want_cache, before, tag="L0"):
-    rep = er.rep.setdefault(tag, {})
-    for k in ("attn_out", "hres", "moe_out", "out"):
-        er.attempt(check_bf16, f"{tag}.{k}", got[k], want[k], rep=rep)
-    er.attempt(check_bf16, f"{tag}.moe_in", got["moe_in"], want["moe_in"], rep=rep, ulps=MOE_IN_ULPS)
-    dl = er.attempt(check_logits, got["logits"], want["logits"], got["moe_in"], want["moe_in"], lw["w_router"],
-                    live, rep=rep)
-    if dl is not None:
-        sel = np.take_along_axis(np.abs(got["logits"].astype(np.float64) - want["logits"]),
-                                 np.maximum(want["ids"], 0), axis=1).max(axis=1)
-        er.attempt(check_routing, got["ids"], got["w"], want["ids"], want["w"], live, sel / 2 + 1e-6, rep=rep)
-    er.attempt(check_records, d, got_cache, want_cache, before, rep=rep)
-
-
 def _case_and_oracle(dsl, name, key):
     sd = _seeded(key)
     layers, dw = _device_weights(dsl, name, sd["weights_seed"])
@@ -140,16 +112,20 @@ def _layer_case(case, l, x_bits):
                                kv=kv, x=x_bits)
 
 
-def _run_decode(dsl, name, key):
+def _run_decode(dsl, name, key, narrow=None):
+    """narrow: the kernel instantiation the step must have launched (None: either)."""
     case, res, caches, live, dw = _case_and_oracle(dsl, name, key)
     dev = dsl.LayerOnDevice(case, weights=dw)
-    _say(f"{key}: decode M={case.M} layers={case.dims.n_layers}")
+    _say(f"{key}: decode M={case.M} layers={case.dims.n_layers} pad rows {int((~live).sum())}")
     got = dev.decode(case.x)
     got_caches = dev.caches_host()
+    ran = dsl.dsl_layer_last_kernel(dw.handle)
     dev.close()
+    if narrow is not None:
+        assert ran == int(narrow), f"{key}: ran the {'narrow' if ran == 1 else 'general'} kernel"
     er = Errors()
-    _check_layer(er, case.dims, case.layers[0], got, res, live, got_caches[0], caches[0], case.kv.cache[0])
-    er.raise_any(key)
+    check_layer(er, case.dims, case.layers[0], got, res, live, got_caches[0], caches[0], case.kv.cache[0])
+    er.raise_any(key, _say)
 
 
 def _run_chain(dsl, name, key):
@@ -167,7 +143,7 @@ def _run_chain(dsl, name, key):
         got = dev.decode(x_in)
         gc = dev.caches_host()[0]
         dev.close()
-        _check_layer(er, d, case.layers[l], got, res["layers"][l], live, gc, caches[l], case.kv.cache[l],
+        check_layer(er, d, case.layers[l], got, res["layers"][l], live, gc, caches[l], case.kv.cache[l],
                      tag=f"L{l}")
         x_in = res["layers"][l]["out"]
 
@@ -228,7 +204,7 @@ def _run_chain(dsl, name, key):
         if not (e <= L * ATOL and c >= COS_MIN):
             er.msgs.append(f"chain {k}: max-abs {e:.4g} (bar {L * ATOL}), cos {c:.7f} on rows whose routing "
                            f"matched")
-    er.raise_any(key)
+    er.raise_any(key, _say)
 
 
 def test_moe_stage_m6_top3(dsl):
@@ -270,7 +246,35 @@ def test_full_layer_m48_top6(dsl):
 
 
 def test_full_layer_m6_top6(dsl):
-    _run_decode(dsl, "layer48", "layer48_m6")
+    _run_decode(dsl, "layer48", "layer48_m6", narrow=True)
+
+
+# Steps of at most 8 rows at the full size take the narrow kernel instantiation (the one
+# the M=6 bench times): 2 and 8 live rows, and 5 and 7 live rows each with a pad row.
+@pytest.mark.parametrize("key", ["layer48_m2", "layer48_m8", "layer48_m6p1", "layer48_m8p1"])
+def test_full_layer_narrow_widths(dsl, key):
+    _run_decode(dsl, "layer48", key, narrow=True)
+
+
+def test_attention_half_m6_pad(dsl):
+    """The attention half alone at the full size on 5 rows of one request and a pad row
+    (the narrow kernel): the pad row gets no record and a zero output."""
+    layers, dw = _device_weights(dsl, "layer48", 7)
+    case = synth.make_case("attn48", 4, n_req=1, rows_per_req=5, n_pad=1, layers=layers)
+    assert case.M == 6 and case.kv.positions[-1] == -1
+    caches = [c.copy() for c in case.kv.cache]
+    want = OL.attn_step(case.dims, layers[0], case.x, case.kv, caches[0])
+    dev = dsl.LayerOnDevice(case, weights=dw)
+    _say("attn6p1: attention step M=6 with a pad row")
+    got = dev.attn(case.x)
+    gc = dev.caches_host()
+    assert dsl.dsl_layer_last_kernel(dw.handle) == 1
+    dev.close()
+    rep = {}
+    assert not got["attn_out"][-1].any()
+    check_bf16("attn_out", got["attn_out"], want["attn_out"], rep)
+    check_records(case.dims, gc[0], caches[0], case.kv.cache[0], rep)
+    _say(f"attn6p1: ok {rep}")
 
 
 # The CPU oracle of three chained layers takes about two minutes at M=48 on the GPU
@@ -279,3 +283,8 @@ def test_full_layer_m6_top6(dsl):
 @pytest.mark.parametrize("M", [1, 6, 12, 16, 17, 24, 36, 48])
 def test_draft_three_layers(dsl, M):
     _run_chain(dsl, "draft", f"draft_m{M}")
+
+
+def test_draft_three_layers_m6_pad(dsl):
+    """Three chained draft layers on 5 rows of one request and a pad row."""
+    _run_chain(dsl, "draft", "draft_m6p1")
