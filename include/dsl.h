@@ -164,6 +164,22 @@ int dsl_decode_step(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_k
                     const int32_t *positions, void *out_bf16, const dsl_taps *taps,
                     void *hip_stream);
 
+/* dsl_decode_step without any allocation, for callers that cannot allocate device
+ * memory at step time: code under HIP graph capture (a width's first dsl_decode_step
+ * allocates its scratch), tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as dsl_decode_step; the step's scratch is a static
+ * device array of 32 MiB per GPU (held until the process ends) instead of the width's
+ * own, and the call makes no hipMalloc, hipFree or other allocating call.  Limit: the
+ * scratch of M rows over dims.n_layers layers must fit 32 MiB (every width up to 48 rows
+ * of one layer at hidden 4096 / 128 experts / inter 2048, or three such layers up to 16
+ * rows); beyond it the call returns DSL_EUNSUPPORTED and launches nothing.  Every handle
+ * on a GPU shares that GPU's array, so two such calls that can overlap on one GPU (two
+ * streams, two threads) race: order them on one stream.  No word of the array is read
+ * before the step writes it, so it needs no clearing between calls. */
+int dsl_decode_step_noalloc(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_kv *kv,
+                            const int32_t *positions, void *out_bf16, const dsl_taps *taps,
+                            void *hip_stream);
+
 /* The attention half of layer 0 only: attn_out = bf16(a), no residual add.  Writes
  * the KV records like a full step. */
 int dsl_attn_step(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_kv *kv,

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1720,6 +1721,30 @@ static int get_width(dsl_layer *L, int M, Scratch *out, long long *stride) {
   return 0;
 }
 
+// The scratch of dsl_decode_step_noalloc: one array per device, which the device holds for
+// as long as the library is loaded.  Host code never passes `scratch` itself to a kernel
+// (on the host that name is a stand-in, not a device address): dsl_layer_build looks up
+// the array's device address on each device once, with that device current, and every
+// launch takes that address.  No word of a step's scratch is read before the step's own
+// launch writes it, so nothing is cleared between calls.
+static constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+static void *g_static_scratch[kMaxDevices];
+static std::mutex g_static_mu;
+
+static int static_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSL_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_scratch[dev]) return 0;
+  void *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(DSL_EHIP, "hipGetSymbolAddress of the static scratch on device %d failed: %s", dev, hipGetErrorString(e));
+  g_static_scratch[dev] = ptr;
+  return 0;
+}
+
 static int check_ptr16(const void *p, const char *what) {
   if (!p) return fail(DSL_EINVAL, "%s is NULL", what);
   if ((uintptr_t)p & 15) return fail(DSL_EINVAL, "%s is not 16-byte aligned", what);
@@ -1749,6 +1774,7 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   HIPCHK(hipGetDeviceProperties(&prop, dev));
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(DSL_EUNSUPPORTED, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
+  if ((rc = static_scratch_init(dev))) return rc;
   int bpc = 0, bpc_narrow = 0;
   HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void *)dsl_layer_kernel<false>, kThreads, 0));
   HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc_narrow, (const void *)dsl_layer_kernel<true>, kThreads, 0));
@@ -1819,7 +1845,7 @@ static int check_kv(const dsl_layer *L, const dsl_kv *kv, int n) {
 }
 
 static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv, const int32_t *pos, void *out,
-                  const dsl_taps *taps, void *stream) {
+                  const dsl_taps *taps, void *stream, bool noalloc = false) {
   if (!L) return fail(DSL_EINVAL, "layer is NULL");
   int rc;
   if ((rc = check_ptr16(x, "input"))) return rc;
@@ -1831,7 +1857,20 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
     if ((rc = check_kv(L, kv, nl))) return rc;
   }
   Params p{};
-  if ((rc = get_width(L, M, &p.s, &p.s_stride))) return rc;
+  if (noalloc) {
+    // the device's static scratch in place of the width's own: no allocation
+    Scratch tmp;
+    const size_t per_layer = layout(L, M, &tmp, nullptr), bytes = per_layer * (size_t)nl;
+    if (bytes > kStaticScratchBytes)
+      return fail(DSL_EUNSUPPORTED, "width %d over %d layer(s) needs %zu bytes of scratch; the no-allocation entry point "
+                  "holds %zu", M, nl, bytes, kStaticScratchBytes);
+    void *base = (L->dev >= 0 && L->dev < kMaxDevices) ? g_static_scratch[L->dev] : nullptr;
+    if (!base) return fail(DSL_EHIP, "the static scratch of device %d was not looked up", L->dev);
+    layout(L, M, &p.s, (char *)base);
+    p.s_stride = (long long)per_layer;
+  } else if ((rc = get_width(L, M, &p.s, &p.s_stride))) {
+    return rc;
+  }
   const dsl_dims &d = L->d;
   p.h = d.hidden; p.H = d.n_heads; p.D = d.head_dim; p.qr = d.q_rank; p.orr = d.o_rank;
   p.W = d.window; p.swa = d.swa_width; p.E = d.n_experts; p.k = d.top_k; p.I = d.inter;
@@ -1863,6 +1902,11 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
 int dsl_decode_step(dsl_layer *L, const void *x, int32_t M, const dsl_kv *kv, const int32_t *pos, void *out,
                     const dsl_taps *taps, void *stream) {
   return launch(L, kModeDecode, x, M, kv, pos, out, taps, stream);
+}
+
+int dsl_decode_step_noalloc(dsl_layer *L, const void *x, int32_t M, const dsl_kv *kv, const int32_t *pos, void *out,
+                            const dsl_taps *taps, void *stream) {
+  return launch(L, kModeDecode, x, M, kv, pos, out, taps, stream, true);
 }
 
 int dsl_attn_step(dsl_layer *L, const void *x, int32_t M, const dsl_kv *kv, const int32_t *pos, void *out,

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.dsl_layer_build.argtypes = [P(Dims), P(Weights), P(c_void_p)]
         L.dsl_layer_reserve.argtypes = [c_void_p, c_int32]
         L.dsl_decode_step.argtypes = [c_void_p, c_void_p, c_int32, P(KV), c_void_p, c_void_p, P(Taps), c_void_p]
+        L.dsl_decode_step_noalloc.argtypes = [c_void_p, c_void_p, c_int32, P(KV), c_void_p, c_void_p, P(Taps),
+                                              c_void_p]
         L.dsl_attn_step.argtypes = [c_void_p, c_void_p, c_int32, P(KV), c_void_p, c_void_p, c_void_p]
         L.dsl_moe_step.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
         L.dsl_layer_health.argtypes = [c_void_p]
@@ -79,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.dsl_layer_destroy.argtypes = [c_void_p]
         L.dsl_layer_destroy.restype = None
         L.dsl_last_error.restype = ctypes.c_char_p
-        for f in ("dsl_layer_build", "dsl_layer_reserve", "dsl_decode_step", "dsl_attn_step", "dsl_moe_step",
+        for f in ("dsl_layer_build", "dsl_layer_reserve", "dsl_decode_step", "dsl_decode_step_noalloc",
+                  "dsl_attn_step", "dsl_moe_step",
                   "dsl_layer_health", "dsl_layer_grid", "dsl_layer_set_trace", "dsl_layer_read_trace",
                   "dsl_layer_last_kernel"):
             getattr(L, f).restype = c_int32
@@ -115,6 +118,13 @@ def dsl_decode_step(h, x: int, M: int, kv: list, positions: int, out: int, taps:
                     stream: int = 0):
     arr = (KV * len(kv))(*kv)
     _check(lib().dsl_decode_step(h, x, M, arr, positions, out, ctypes.byref(taps) if taps else None, stream))
+
+
+def dsl_decode_step_noalloc(h, x: int, M: int, kv: list, positions: int, out: int, taps: Taps | None = None,
+                            stream: int = 0):
+    arr = (KV * len(kv))(*kv)
+    _check(lib().dsl_decode_step_noalloc(h, x, M, arr, positions, out, ctypes.byref(taps) if taps else None,
+                                         stream))
 
 
 def dsl_attn_step(h, x: int, M: int, kv: list, positions: int, out: int, stream: int = 0):
@@ -246,8 +256,9 @@ class LayerOnDevice:
     def new_bf16(self, M: int):
         return self.torch.zeros((M, self.dims.hidden), dtype=self.torch.int16, device=self.dev)
 
-    def decode(self, x_bits: np.ndarray, taps: bool = True) -> dict:
-        """One decode step on x (bf16 codes); returns host copies of the outputs."""
+    def decode(self, x_bits: np.ndarray, taps: bool = True, noalloc: bool = False) -> dict:
+        """One decode step on x (bf16 codes); returns host copies of the outputs.  noalloc:
+        through dsl_decode_step_noalloc."""
         torch = self.torch
         M = x_bits.shape[0]
         x = self._up(x_bits.view(np.int16))
@@ -265,8 +276,9 @@ class LayerOnDevice:
             t = Taps(res["attn_out"].data_ptr(), res["hres"].data_ptr(), res["moe_in"].data_ptr(),
                      res["moe_out"].data_ptr(), res["ids"].data_ptr(), res["w"].data_ptr(),
                      res["logits"].data_ptr(), res["layer_ids"].data_ptr())
-        dsl_decode_step(self.handle, x.data_ptr(), M, self.kv_structs, self.positions.data_ptr(),
-                        out.data_ptr(), t, self.stream())
+        step = dsl_decode_step_noalloc if noalloc else dsl_decode_step
+        step(self.handle, x.data_ptr(), M, self.kv_structs, self.positions.data_ptr(), out.data_ptr(), t,
+             self.stream())
         torch.cuda.synchronize(self.dev)
         _check(dsl_layer_health(self.handle))
         return self._host(res)
