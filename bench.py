@@ -10,8 +10,8 @@ and their load change from step to step; each step's algorithmic bytes are count
 from its own expert ids.
 
 Prints one JSON line: the M=6 full layer (top-6 of 128 experts) as the headline,
-the M=48 layer and the three chained draft layers at M=6 (top-3, per layer) as
-further points, the roofline of the launch (algorithmic HBM bytes per step over the
+the M=48 layer, the three chained draft layers at M=6 (top-3, per layer) and the
+layer with A8W4 experts (MXFP8 activations) at M=6 and M=48 as further points, the roofline of the launch (algorithmic HBM bytes per step over the
 measured kernel time against 8 TB/s, and against a plain device copy's measured
 rate), the M=6 layer with warm weights (one copy; labelled, not the headline), and the
 CPU oracle timed on a bounded sample.  Each point also gives the wall
@@ -331,6 +331,16 @@ def main():
         draft = run_point(dsl, torch, "draft", 6, 2, args.steps, args.warmup, weights * 3,
                           graph_replay=not args.no_graph)
         print(f"[bench] draft M=6: {draft['us_per_layer_kernel']:.1f} us/layer, {draft['gbs']:.0f} GB/s", flush=True)
+    m6_a8 = m48_a8 = None
+    if not args.only_m6:
+        # the A8W4 variant: MXFP8 activations into the same MXFP4 experts (same weights)
+        print("[bench] A8W4 experts: M=6 and M=48 full layer", flush=True)
+        m6_a8 = run_point(dsl, torch, "layer48_a8", 6, args.copies, args.steps, args.warmup, weights,
+                          graph_replay=False)
+        m48_a8 = run_point(dsl, torch, "layer48_a8", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
+                           graph_replay=False)
+        print(f"[bench] A8W4 M=6: {m6_a8['us_kernel_mean']:.1f} us/launch; M=48: {m48_a8['us_kernel_mean']:.1f} "
+              f"us/launch", flush=True)
     warm = None
     if not args.only_m6:
         # one weight copy for every launch: what stays in the 256 MB Infinity Cache between
@@ -368,6 +378,8 @@ def main():
         "m6": m6,
         "m48": m48,
         "draft_m6": draft,
+        "a8w4_m6": m6_a8,
+        "a8w4_m48": m48_a8,
         "warm_m6": warm,
         "cpu_baseline": cpu,
     }

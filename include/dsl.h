@@ -66,6 +66,7 @@ extern "C" {
  * 128; the shared expert has 128x128 scale blocks); head_dim in {64, 128, 256,
  * 512}; 1 <= n_experts <= 128; 1 <= top_k <= min(8, n_experts);
  * 1 <= max_rows <= 48; 1 <= n_layers <= DSL_MAX_LAYERS; 1 <= window <= 256;
+ * expert_a8 in {0, 1};
  * 0 <= swa_width <= 256 (a row's keys are split over at most 8 waves of 32 keys);
  * kv_block >= 1.  Other values: DSL_EUNSUPPORTED or DSL_EINVAL. */
 typedef struct {
@@ -81,6 +82,11 @@ typedef struct {
   int32_t kv_block;    /* B, tokens per cache block                             */
   int32_t max_rows;    /* largest step width                                    */
   int32_t n_layers;    /* chained layers per step (3 for the draft model)       */
+  int32_t expert_a8;   /* 0: the routed experts take the bf16 MoE input (W4A16);
+                          1: they take MXFP8 activations (A8W4, the pages' "a8w4
+                          MoE": PR 60397, Test Plan): gate/up reads MXq(u) and down
+                          reads MXq(z), each per 1x32 block of the bf16 value.  The
+                          router and the shared expert keep the bf16 u.           */
   float norm_eps;      /* RMSNorm epsilon (1e-6)                                */
   float swiglu_limit;  /* SwiGLU clamp (7.0)                                    */
 } dsl_dims;

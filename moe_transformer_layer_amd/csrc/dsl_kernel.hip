@@ -508,6 +508,32 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
 
 // ============================================================== MoE
 
+// MXFP8 of 32-element blocks of bf16 rows, kept as exact bf16 values: block b of n
+// blocks (row b / per, 32 columns from 32 (b % per)) from src to dst, one thread per block.
+// The A8W4 variant's expert inputs: "Mono decode layer for DeepSeek-V4.1-Flash on MI355X"
+// (vLLM PR 60397), Test Plan (the a8w4 MoE), with the OCP MX block rule of the layer's other
+// MXFP8 activations.
+__device__ __forceinline__ void mx_block_bf16(const uint16_t *src, uint16_t *dst, int b, int per, int ld) {
+  const size_t off = (size_t)(b / per) * ld + 32 * (b % per);
+  float v[32];
+  load_bf16<32>(src + off, v);
+  mx_quant_dequant<32>(v);
+  store_bf16<32>(dst + off, v);
+}
+
+// A8W4: MXFP8 of the MoE input u [M][h] into uq, by the grid's threads in reverse order (the
+// last waves, which have no router or shared gate/up task, take the blocks first).
+__device__ __forceinline__ void st_u_quant(const Params &p, const Ctx &cx, const uint16_t *u) {
+  const int per = p.h >> 5, n = p.M * per, nt = cx.nw * kWave;
+  for (int b = nt - 1 - (cx.gw * kWave + cx.lane); b < n; b += nt) mx_block_bf16(u, p.s.uq, b, per, p.h);
+}
+
+// A8W4: MXFP8 of the routed SwiGLU outputs z [pairs][I] into zq (one thread per block).
+__device__ __forceinline__ void st_z_quant(const Params &p, const Routing &R) {
+  const int per = p.I >> 5, n = R.np * per;
+  for (int b = bid() * kThreads + tid(); b < n; b += gridDim.x * kThreads) mx_block_bf16(p.s.zr, p.s.zq, b, per, p.I);
+}
+
 // Router partial logits of one (expert e, K chunk c) task for all rows: lane l takes
 // elements c kc + 512 j + 8 l .. + 8 (j < kc / 512, lanes past the chunk idle), the
 // lane partials of 8 rows at a time are summed across the wave by the transposing
@@ -582,6 +608,7 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
                                            p.M, p.s.p_sh);
     }
   }
+  if (p.a8) st_u_quant(p, cx, u);
 }
 
 // Top-k of one row's router logits (one wave; two experts per lane, v0 for expert lane
@@ -703,6 +730,8 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     const int tot0 = __shfl(s0, kWave - 1, kWave);
     R.start[lane] = s0 - c0;
     R.start[lane + 64] = tot0 + s1 - c1;
+    const int tot1 = __shfl(s1, kWave - 1, kWave);
+    if (lane == 0) R.np = tot0 + tot1;
     // the distinct experts: in id order for a step of at most 8 rows; wider steps take
     // the experts with more rows first (then by id), so that the round-robin task order
     // gives every wave an even share of the matrix-core experts
@@ -798,6 +827,7 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
   const int i = lane & 15, g = lane >> 4, I = p.I, h = p.h;
   const uint8_t *W = w.ex_wd + (size_t)e * h * (I >> 1);
   const uint8_t *S8 = w.ex_wd_s + (size_t)e * h * (I >> 5);
+  const uint16_t *zin = p.a8 ? p.s.zq : p.s.zr;
   const uint16_t *xrow[NCG];
   bool xok[NCG];
   v4f acc[NT][NCG];
@@ -805,7 +835,7 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
   for (int c = 0; c < NCG; c++) {
     const int j = 16 * c + i;
     xok[c] = j < ce;
-    xrow[c] = p.s.zr + (size_t)(p0 + (xok[c] ? j : 0)) * I;
+    xrow[c] = zin + (size_t)(p0 + (xok[c] ? j : 0)) * I;
 #pragma unroll
     for (int tt = 0; tt < NT; tt++) acc[tt][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -967,9 +997,10 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   const size_t row_bytes = (size_t)I >> 1;
   const uint8_t *W = w.ex_wd + (size_t)e * h * row_bytes;
   const uint8_t *S = w.ex_wd_s + (size_t)e * h * NB;
+  const uint16_t *zin = p.a8 ? p.s.zq : p.s.zr;
   const uint16_t *rows[CE];
 #pragma unroll
-  for (int m = 0; m < CE; m++) rows[m] = p.s.zr + (size_t)(p0 + (m < ce ? m : 0)) * I;
+  for (int m = 0; m < CE; m++) rows[m] = zin + (size_t)(p0 + (m < ce ? m : 0)) * I;
   uint32_t xv[Q][CE][16];
   valu_load_x<CE, Q>(rows, lane, xv);
   v4u sc[NR / 16][Q];
@@ -1334,13 +1365,14 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ unsigned tq_base[kWavesPerBlock];  // each wave's wo_a group counter before this layer
   __shared__ unsigned cb_base[kWavesPerBlock];  // each wave's combine group counter before this layer
   const unsigned nb = gridDim.x;
-  int mode, n_layers;
+  int mode, n_layers, a8;
   SyncWords *sw;
   Tracer tr;
   {
     KParams *kp = kparams();
     mode = kp->mode;
     n_layers = kp->n_layers;
+    a8 = kp->a8;
     sw = kp->sync;
     tr.buf = kp->trace;
   }
@@ -1514,12 +1546,19 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     tr.mark();
     {
       STAGE(l);
-      st_routed_gate_up<NARROW>(p, cx, w, R, moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
+      st_routed_gate_up<NARROW>(p, cx, w, R, p.a8 ? p.s.uq : moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
       // the shared SwiGLU, off the critical path: its reader, the shared down projection,
       // comes after the next grid barrier
       st_shared_swiglu(p, moe_mode);
     }
     SYNC();
+    if (a8) {
+      {
+        STAGE(l);
+        st_z_quant(p, R);
+      }
+      SYNC();
+    }
     bool cfold;
     {
       STAGE(l);
@@ -1652,6 +1691,7 @@ static int validate_dims(const dsl_dims *d) {
     return fail(DSL_EUNSUPPORTED, "window %d / swa_width %d: at most %d keys per row (8 splits of %d)", d->window,
                 d->swa_width, 8 * kSplitKeys, kSplitKeys);
   if (d->kv_block < 1) return fail(DSL_EINVAL, "kv_block %d < 1", d->kv_block);
+  if (d->expert_a8 != 0 && d->expert_a8 != 1) return fail(DSL_EINVAL, "expert_a8 %d is neither 0 nor 1", d->expert_a8);
   if (!(d->norm_eps >= 0.f) || !(d->swiglu_limit > 0.f))
     return fail(DSL_EINVAL, "norm_eps must be >= 0 and swiglu_limit > 0");
   return 0;
@@ -1697,6 +1737,8 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   s->zr = (uint16_t *)take(m * k * I * 2);
   s->y = (float *)take(m * k * h * 4);
   s->p_shd = (float *)take((Is / pl.kc_shd) * m * h * 4);
+  s->uq = d.expert_a8 ? (uint16_t *)take(m * h * 2) : nullptr;
+  s->zq = d.expert_a8 ? (uint16_t *)take(m * k * I * 2) : nullptr;
   return (off + 255) & ~(size_t)255;
 }
 
@@ -1874,7 +1916,7 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   const dsl_dims &d = L->d;
   p.h = d.hidden; p.H = d.n_heads; p.D = d.head_dim; p.qr = d.q_rank; p.orr = d.o_rank;
   p.W = d.window; p.swa = d.swa_width; p.E = d.n_experts; p.k = d.top_k; p.I = d.inter;
-  p.Is = d.shared_inter; p.B = d.kv_block; p.n_layers = nl;
+  p.Is = d.shared_inter; p.B = d.kv_block; p.n_layers = nl; p.a8 = d.expert_a8;
   p.eps = d.norm_eps; p.lim = d.swiglu_limit;
   p.attn_scale = 1.0f / sqrtf((float)d.head_dim);
   p.M = M; p.mode = mode; p.S = L->S; p.pl = L->plan;

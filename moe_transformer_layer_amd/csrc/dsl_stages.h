@@ -58,10 +58,13 @@ struct Scratch {
   uint16_t *zr;            // bf16 routed SwiGLU output per (row, slot) pair [M*k][I]
   float *y;                // routed expert outputs per pair [M*k][h]
   float *p_shd;            // [nks][M][h]
+  uint16_t *uq;            // A8W4: MXFP8(u) as exact bf16 values [M][h], the routed gate/up input
+  uint16_t *zq;            // A8W4: MXFP8(z) as exact bf16 values [M*k][I], the routed down input
 };
 
 struct Params {
   int h, H, D, qr, orr, W, swa, E, k, I, Is, B, n_layers;
+  int a8;  // the routed experts take MXFP8 activations (A8W4)
   float eps, lim, attn_scale;
   int M, mode, S;
   Plan pl;
@@ -86,6 +89,7 @@ struct Routing {
   unsigned long long rows[128];    // rows that selected each expert (bit m)
   int cnt[128], start[128], list[128];
   int nd;
+  int np;  // (row, slot) pairs routed (live rows times k)
 };
 
 struct Ctx {

@@ -31,7 +31,7 @@ class DslError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("hidden", "n_heads", "head_dim", "q_rank", "o_rank", "window",
                                        "swa_width", "n_experts", "top_k", "inter", "shared_inter",
-                                       "kv_block", "max_rows", "n_layers")] + \
+                                       "kv_block", "max_rows", "n_layers", "expert_a8")] + \
                [("norm_eps", c_float), ("swiglu_limit", c_float)]
 
 
@@ -97,7 +97,7 @@ def _check(rc: int):
 
 def dims_struct(d) -> Dims:
     return Dims(d.hidden, d.n_heads, d.head_dim, d.q_rank, d.o_rank, d.window, d.swa_width, d.n_experts,
-                d.top_k, d.inter, d.shared_inter, d.kv_block, d.max_rows, d.n_layers, d.norm_eps,
+                d.top_k, d.inter, d.shared_inter, d.kv_block, d.max_rows, d.n_layers, d.expert_a8, d.norm_eps,
                 d.swiglu_limit)
 
 

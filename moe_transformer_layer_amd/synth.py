@@ -41,6 +41,7 @@ class Dims:
     kv_block: int
     max_rows: int
     n_layers: int = 1
+    expert_a8: int = 0  # 1: the routed experts take MXFP8 activations (A8W4)
     norm_eps: float = 1e-6
     swiglu_limit: float = 7.0
 
@@ -78,6 +79,15 @@ CONFIGS = {
                       swa_width=64, n_experts=16, top_k=3, inter=256, shared_inter=256,
                       kv_block=16, max_rows=13, n_layers=2),
 }
+# The same workloads with MXFP8 activations into the MXFP4 experts (A8W4); each draws
+# the same weights and inputs as the workload it is named after.
+for _n in ("moe6", "layer48", "mid"):
+    CONFIGS[_n + "_a8"] = CONFIGS[_n].replace(expert_a8=1)
+
+
+def base_name(name: str) -> str:
+    """The workload whose draws a configuration shares (an _a8 variant's base)."""
+    return name[:-3] if name.endswith("_a8") else name
 
 
 def _bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -258,7 +268,7 @@ def make_weights(name: str, weights_seed: int, n_layers: int | None = None, gate
     if n_layers is not None:
         d = d.replace(n_layers=n_layers)
     rng = np.random.default_rng([weights_seed, 0])
-    return [gen_layer_weights(d, rng, attn_amp=0.05 if name == "tiny" else None, gate_gain=gate_gain)
+    return [gen_layer_weights(d, rng, attn_amp=0.05 if base_name(name) == "tiny" else None, gate_gain=gate_gain)
             for _ in range(d.n_layers)]
 
 
@@ -278,6 +288,7 @@ def make_case(name: str, seed: int, M: int | None = None, n_pad: int = 0,
         layers = make_weights(name, seed if weights_seed is None else weights_seed, n_layers, gate_gain)
     assert len(layers) == d.n_layers
     rng = np.random.default_rng([seed, 1])
+    name = base_name(name)
     if name == "moe6":
         M = M or 6
         x = gen_x(d, rng, M, truncate=None)

@@ -194,17 +194,32 @@ def attn_half(d, lw: dict, x_bits: np.ndarray, kv, cache: np.ndarray) -> dict:
     return dict(a=a, q=q, o=o, t=t, q_lat=q_lat, kv_n=kv_n, records=recs)
 
 
+def mxq(v: np.ndarray) -> np.ndarray:
+    """MXFP8 quantization per 1x32 block along the last axis, returned as the dequantized
+    values (e4m3 code times the block's 2^(X-127)): the activation side of an MXFP8
+    linear."""
+    return mx_e4m3_dequant_act(*mx_e4m3_quantize(v))
+
+
 def moe_half(d, lw: dict, u_bits: np.ndarray, live: np.ndarray | None = None) -> dict:
     """MoE on rows u (bf16 codes, already normalized): f32 router logits, top-k with
     renormalized weights, the FP8 shared expert (128x128 f32 block scales, bf16 input),
     the selected MXFP4 experts, and the float32 combine m = shared + sum_j w_j y_j in
     fixed order (shared first, then slots in emission order).  Rows with live False are
-    not routed (ids -1, weights 0, m = 0)."""
+    not routed (ids -1, weights 0, m = 0).
+
+    With d.expert_a8 set (the "a8w4 MoE" of the pages' deployments: "Mono decode layer
+    for DeepSeek-V4.1-Flash on MI355X", vLLM PR 60397, Test Plan) the routed experts take
+    MXFP8 activations: the gate/up input is MXq(u) and the down input MXq(z), each
+    quantized per 1x32 block from its bf16 value (u and z stay bf16, R6 and R7).  The
+    router and the shared expert keep the bf16 u."""
     M = u_bits.shape[0]
     I, Is = d.inter, d.shared_inter
+    a8 = bool(getattr(d, "expert_a8", 0))
     if live is None:
         live = np.ones(M, dtype=bool)
     u = bf16_value(u_bits)
+    u_ex = mxq(u) if a8 else u
     logits = f32(u @ np.asarray(lw["w_router"], dtype=np.float64).T)
     ids, w = router_topk(logits, d.top_k)
     ids[~live] = -1
@@ -221,9 +236,9 @@ def moe_half(d, lw: dict, u_bits: np.ndarray, live: np.ndarray | None = None) ->
                 pairs.setdefault(int(ids[m, j]), []).append((m, j))
     for e, pl in sorted(pairs.items()):
         rows = [m for m, _ in pl]
-        gu_e = f32(gemv_mxfp4(lw["ex_w13"][e], lw["ex_w13_s"][e], u[rows]))
+        gu_e = f32(gemv_mxfp4(lw["ex_w13"][e], lw["ex_w13_s"][e], u_ex[rows]))
         z = bf16_round(swiglu_clamp(gu_e[:, :I], gu_e[:, I:], d.swiglu_limit))
-        ye = f32(gemv_mxfp4(lw["ex_wd"][e], lw["ex_wd_s"][e], z))
+        ye = f32(gemv_mxfp4(lw["ex_wd"][e], lw["ex_wd_s"][e], mxq(z) if a8 else z))
         for (m, j), yy in zip(pl, ye):
             y[m, j] = yy
     mo = ys.copy()

@@ -37,6 +37,11 @@ CASES = {
     "layer48_m6p1": ("layer48", 7, dict(n_req=1, rows_per_req=5, n_pad=1), "decode"),
     "layer48_m8p1": ("layer48", 7, dict(n_req=1, rows_per_req=7, n_pad=1), "decode"),
     "draft_m6p1": ("draft", 11, dict(n_req=1, rows_per_req=5, n_pad=1), "decode"),
+    # A8W4 experts (MXFP8 activations): the router sees the same bf16 input, so the gap
+    # rule picks what it picks for the W4A16 workload of the same draws
+    "moe6_a8": ("moe6_a8", 5, dict(), "moe"),
+    "layer48_a8_m48": ("layer48_a8", 7, dict(M=48), "decode"),
+    "layer48_a8_m6": ("layer48_a8", 7, dict(M=6), "decode"),
     # the graph replay stress: both of its input sets (the case's x, and a second draw)
     "stress_m48": ("layer48", 5, dict(M=48), "stress"),
     "stress_m6": ("layer48", 5, dict(M=6), "stress"),

@@ -36,7 +36,7 @@ def test_header_structs_match_binding():
     body = body[: body.index("} dsl_weights;")]
     names = re.findall(r"\*\s*([a-z0-9_]+)", body)
     assert tuple(names) == dsl.WEIGHT_FIELDS
-    assert ctypes.sizeof(dsl.Dims) == 16 * 4
+    assert ctypes.sizeof(dsl.Dims) == 17 * 4
     assert ctypes.sizeof(dsl.KV) == 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
 
 

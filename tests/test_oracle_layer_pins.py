@@ -187,14 +187,16 @@ def torch_layer(d, lw, x_bits, kv, cache):
     gu = _f32r(u @ _w_b128(lw["sh_w13"], lw["sh_w13_s"]).T)
     zs = _bf16r(_swiglu(gu[:, :Is], gu[:, Is:], d.swiglu_limit))
     m = _f32r(zs @ _w_b128(lw["sh_wd"], lw["sh_wd_s"]).T)
+    # A8W4: the routed experts' inputs (u, and the SwiGLU output z) go through MXFP8
+    act = _mxq if d.expert_a8 else (lambda v: v)
     for j in range(k):
         for r in range(M):
             if not live[r]:
                 continue
             e = int(ids[r, j])
-            g = _f32r(u[r:r + 1] @ _w_fp4(lw["ex_w13"][e], lw["ex_w13_s"][e]).T)
+            g = _f32r(act(u[r:r + 1]) @ _w_fp4(lw["ex_w13"][e], lw["ex_w13_s"][e]).T)
             z = _bf16r(_swiglu(g[:, :I], g[:, I:], d.swiglu_limit))
-            y = _f32r(z @ _w_fp4(lw["ex_wd"][e], lw["ex_wd_s"][e]).T)
+            y = _f32r(act(z) @ _w_fp4(lw["ex_wd"][e], lw["ex_wd_s"][e]).T)
             m[r] = m[r] + wt[r, j] * y[0]
     m = _f32r(m)
     m[~live] = 0
@@ -244,6 +246,8 @@ def mismatches(d, orc, case) -> list:
 _CASES = {
     # causal window over a paged cache, two requests of 6 rows and a pad row
     "mid": dict(name="mid", seed=21, n_pad=1),
+    # the same with MXFP8 activations into the routed experts (A8W4)
+    "mid_a8": dict(name="mid_a8", seed=21, n_pad=1),
     # index-table rows, two chained layers (layer 1's input is layer 0's output)
     "mid_draft": dict(name="mid_draft", seed=22),
 }
@@ -295,6 +299,37 @@ _SLIPS = {
     "x instead of hres in the output": [('out_bits = bf16_encode(hres + mo["m"])',
                                          'out_bits = bf16_encode(x + mo["m"])')],
 }
+
+
+_A8_SLIPS = {
+    "a8: gate/up input not quantized": [("u_ex = mxq(u) if a8 else u", "u_ex = u")],
+    "a8: down input not quantized": [('lw["ex_wd_s"][e], mxq(z) if a8 else z))', 'lw["ex_wd_s"][e], z))')],
+}
+
+
+@pytest.mark.parametrize("slip", list(_A8_SLIPS))
+def test_planted_a8_slip_fails_the_pin(slip):
+    c = _case("mid_a8")
+    bad = mismatches(c.dims, _mutant(_A8_SLIPS[slip]), c)
+    assert bad, f"planted slip '{slip}' passed the composition pin"
+
+
+def test_a8_changes_only_the_routed_experts():
+    """A8W4 and W4A16 on the same draws: the attention half, the MoE input, the router and
+    the KV records are identical; the MoE output differs (the experts' inputs are
+    quantized), by no more than the MXFP8 rounding of their inputs allows."""
+    c16, c8 = _case("mid"), _case("mid_a8")
+    assert np.array_equal(c16.x, c8.x)
+    r16 = L.decode_step(c16.dims, c16.layers, c16.x, c16.kv, [x.copy() for x in c16.kv.cache])
+    r8 = L.decode_step(c8.dims, c8.layers, c8.x, c8.kv, [x.copy() for x in c8.kv.cache])
+    for key in ("attn_out", "hres", "moe_in", "ids", "logits"):
+        np.testing.assert_array_equal(r16[key], r8[key])
+    from oracle.formats import bf16_value
+    a, b = bf16_value(r16["moe_out"]), bf16_value(r8["moe_out"])
+    assert (a != b).any()
+    # e4m3 keeps 4 significant bits: each quantized input is within 2^-4 of its value, so
+    # the branch moves by a few percent of its size, not more
+    assert np.abs(a - b).max() < 0.1 * np.abs(a).max()
 
 
 def test_unmutated_copy_passes():

@@ -3,7 +3,8 @@ inter 2048), in the launch configuration the bench times, against the oracle on 
 same seeded inputs.  Seeds come from tests/golden/seeds.json (written by
 make_seeds.py with the oracle alone); each test re-checks the top-k gap rule.
 
-  MoE stage alone, M = 6, top-3                 (moe6)
+  MoE stage alone, M = 6, top-3, W4A16 and A8W4 (moe6, moe6_a8)
+  full layer with A8W4 experts, M = 48 and M = 6 (layer48_a8)
   attention half alone, M = 48 (8 x 6 rows)     (attn48)
   full layer, top-6, M = 48 and M = 6           (layer48)
   full layer at the narrow kernel's widths: 2, 8, 5 + a pad row, 7 + a pad row
@@ -207,21 +208,22 @@ def _run_chain(dsl, name, key):
     er.raise_any(key, _say)
 
 
-def test_moe_stage_m6_top3(dsl):
-    sd = _seeded("moe6")
-    layers, dw = _device_weights(dsl, "moe6", sd["weights_seed"])
-    case = synth.make_case("moe6", sd["seed"], layers=layers)
+@pytest.mark.parametrize("name", ["moe6", "moe6_a8"])
+def test_moe_stage_m6_top3(dsl, name):
+    sd = _seeded(name)
+    layers, dw = _device_weights(dsl, name, sd["weights_seed"])
+    case = synth.make_case(name, sd["seed"], layers=layers)
     d = case.dims
     want = OL.moe_step(d, layers[0], case.x)
     assert float(OL.topk_gap(want["logits"], d.top_k).min()) >= GAP_MIN
     dev = dsl.LayerOnDevice(case, weights=dw)
-    _say("moe6: moe step M=6")
+    _say(f"{name}: moe step M=6")
     got = dev.moe(case.x)
     dev.close()
     rep = {}
     check_bf16("moe_out", got["moe_out"], want["moe_out"], rep)
     check_routing(got["ids"], got["w"], want["ids"], want["w"], np.ones(case.M, bool), W_TOL_MOE, rep)
-    _say(f"moe6: ok {rep}")
+    _say(f"{name}: ok {rep}")
 
 
 def test_attention_half_m48(dsl):
@@ -283,6 +285,13 @@ def test_attention_half_m6_pad(dsl):
 @pytest.mark.parametrize("M", [1, 6, 12, 16, 17, 24, 36, 48])
 def test_draft_three_layers(dsl, M):
     _run_chain(dsl, "draft", f"draft_m{M}")
+
+
+# A8W4: MXFP8 activations into the routed experts, the full layer at 48 and at 6 rows
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M", [48, 6])
+def test_full_layer_a8(dsl, M):
+    _run_decode(dsl, "layer48_a8", f"layer48_a8_m{M}", narrow=M <= 8)
 
 
 def test_draft_three_layers_m6_pad(dsl):

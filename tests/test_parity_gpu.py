@@ -85,6 +85,15 @@ def test_mid_draft_two_layers(dsl):
     run_decode(dsl, case, res, caches, W_TOL_LAYER)
 
 
+# A8W4 (MXFP8 activations into the routed experts) either side of 8 rows, with a pad row
+@pytest.mark.parametrize("n_req,rows,n_pad", [(1, 6, 1), (2, 6, 0)])
+def test_mid_layer_a8(dsl, n_req, rows, n_pad):
+    case, (res, caches) = _decode_case("mid_a8", f"mid_a8_{n_req}x{rows}+{n_pad}", first=800,
+                                       n_req=n_req, rows_per_req=rows, n_pad=n_pad)
+    assert case.dims.expert_a8 == 1
+    run_decode(dsl, case, res, caches, W_TOL_LAYER)
+
+
 def test_mid_attention_only(dsl):
     case = synth.make_case("mid", 400, n_pad=1)
     caches = [c.copy() for c in case.kv.cache]
@@ -100,18 +109,19 @@ def test_mid_attention_only(dsl):
     check_records(case.dims, gc[0], caches[0], case.kv.cache[0])
 
 
-def test_mid_moe_only(dsl):
-    d = synth.CONFIGS["mid"]
+@pytest.mark.parametrize("name", ["mid", "mid_a8"])
+def test_mid_moe_only(dsl, name):
+    d = synth.CONFIGS[name]
 
     def make(s):
-        c = synth.make_case("mid", s)
+        c = synth.make_case(name, s)
         return c
 
     def run(c):
         r = OL.moe_step(d, c.layers[0], c.x)
         return r, [r]
 
-    case, res = gap_seed("mid", "mid_moe", make, run, lambda c: np.ones(c.M, bool), first=500)
+    case, res = gap_seed(name, f"{name}_moe", make, run, lambda c: np.ones(c.M, bool), first=500)
     dev = dsl.LayerOnDevice(case)
     try:
         _say(f"moe mid M={case.M}")
