@@ -1068,8 +1068,11 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
   const int T = R.nd * tiles_n;
   const int qv = NARROW ? 2 : p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   for (int t = cx.gw, base = 0; t < T; base += cx.nw, t = later_round_task(cx, base, T)) {
-    const int q = t / tiles_n, tile = t - q * tiles_n;
-    const int e = R.list[q], ce = R.cnt[e], p0 = R.start[e];
+    // wave-uniform: keep them (and the addresses built on them) in scalar registers
+    const int tu = __builtin_amdgcn_readfirstlane(t);
+    const int q = tu / tiles_n, tile = tu - q * tiles_n;
+    const int e = __builtin_amdgcn_readfirstlane(R.list[q]);
+    const int ce = __builtin_amdgcn_readfirstlane(R.cnt[e]), p0 = __builtin_amdgcn_readfirstlane(R.start[e]);
     const int ncg = NARROW ? 1 : (ce + 15) >> 4;
     if (qv && ce <= 2) {
       if (!NARROW && qv == 1) {
