@@ -287,11 +287,42 @@ struct SyncWords {
   unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
   unsigned tq[64][16];      // wo_a tasks finished per 32-column group of t; only grow
   unsigned cb[128][16];     // down-stage waves finished per 32-column group of the MoE output; only grow
+  unsigned ho[80][64];      // producer hand-off counters (kHo* below); only grow
   unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };
 
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
+
+// Hand-off counters: finished producers of one consumer set, counted after each producer's
+// stores have drained.  kHoQ .. +7: q rows (one copy per group of blocks, so the pollers
+// spread over 8 lines); kHoKv: kv records and key-offset rows; kHoQb + h: wq_b tasks of head
+// h; kHoAtt + h: attention items of head h.
+enum : int { kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoSlots = 73, kHoHeads = 32 };
+
+// Waits until counter id reaches target (modular, like the barrier's release word): lane 0
+// polls, the wave follows.  Bounded like the barrier's spin: a count that never arrives
+// records kFaultBarrier and lets the wave go on, so the launch always drains.
+__device__ __forceinline__ void ho_wait(SyncWords *sw, int id, unsigned target, int lane) {
+  if (lane == 0) {
+    unsigned spins = 0;
+    while ((int)(__hip_atomic_load(gptr(&sw->ho[id][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1u << 24)) {
+        __hip_atomic_fetch_or(gptr(&sw->health), (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");  // the consumer's loads stay after the wait
+}
+
+// Counts one finished producer on counter id: the wave's stores are drained first, so the
+// counted data are at the coherence point before any consumer can see the count.
+__device__ __forceinline__ void ho_count(SyncWords *sw, int id, int lane, unsigned n = 1) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0) __hip_atomic_fetch_add(gptr(&sw->ho[id][0]), n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Barriers completed on this sync state before the launch.  Every block reads it before
 // its first arrival, and no barrier of the launch completes before all blocks have

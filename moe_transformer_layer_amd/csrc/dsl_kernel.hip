@@ -13,6 +13,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -207,6 +208,15 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
           break;
       }
     }
+    if (p.ho && b < 3 * p.M) {
+      // hand-off: the row's stores drained in every wave, then one count (a q row on all
+      // eight copies of its counter; a kv record or a key-offset row on kHoKv)
+      barrier_drain();
+      __syncthreads();
+      if (tid() < (b < p.M ? 8 : 1))
+        __hip_atomic_fetch_add(gptr(&p.sync->ho[b < p.M ? kHoQ + tid() : kHoKv][0]), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
   for (int m = bid(); m < p.M; m += gridDim.x) {
@@ -336,8 +346,13 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
 // splits' partials meet in LDS (lds: 8 D + 16 floats), where one wave per item combines
 // them, quantizes the output to MXFP8 (a 32-block spans 32 / V lanes) and stores it.
 // Pad rows give zeros.
+// Hand-off targets of layer l: each counter grows by a fixed number per layer, read relative
+// to its value at the start of the launch (hb, in LDS)
+__device__ __forceinline__ unsigned ho_per_qb(const Params &p) { return (unsigned)((p.D >> 4) * (p.qr / p.pl.kc_qb)); }
+
 template <int V>
-__device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds) {
+__device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds,
+                                               const unsigned *hb, int l) {
   const int S = p.S, D = p.D;
   const int T = p.M * p.H;
   // items per block: one when the grid has a block per item (the item's split waves then
@@ -349,16 +364,21 @@ __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, c
     const int t = t0 + i;
     if (i < P && t < T) {
       const int m = t / p.H, hh = t - m * p.H;
-      float mx = -INFINITY, l = 0.f, o[V];
+      float mx = -INFINITY, l_ = 0.f, o[V];
 #pragma unroll
       for (int v = 0; v < V; v++) o[v] = 0.f;
+      if (p.ho) {
+        // the head's q (every wq_b task of its columns) and the step's records and key offsets
+        ho_wait(p.sync, kHoQb + hh, hb[kHoQb + hh] + (unsigned)(l + 1) * ho_per_qb(p), lane);
+        ho_wait(p.sync, kHoKv, hb[kHoKv] + (unsigned)(l + 1) * (unsigned)(2 * p.M), lane);
+      }
       // a pad row's key offsets are all -1, so its item gives zeros
-      attn_item<V>(p, kv, m, hh, sp, lane, mx, l, o);
+      attn_item<V>(p, kv, m, hh, sp, lane, mx, l_, o);
 #pragma unroll
       for (int v = 0; v < V; v++) lo_[w * D + lane * V + v] = o[v];
       if (lane == 0) {
         lml[2 * w] = mx;
-        lml[2 * w + 1] = l;
+        lml[2 * w + 1] = l_;
       }
     }
     __syncthreads();
@@ -384,6 +404,7 @@ __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, c
       }
       mx_quant_dequant<V>(o);
       store_bf16<V>(p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + lane * V, o);
+      if (p.ho) ho_count(p.sync, kHoAtt + hh, lane);
     }
     __syncthreads();
   }
@@ -445,11 +466,52 @@ __device__ __forceinline__ void tq_group_quant(const Params &p, int j, int lane)
   }
 }
 
+// Hand-off: wo_a's K chunk ks holds heads [ks kc / D, (ks + 1) kc / D) of the attention output;
+// wait until every row's item of each has been stored
+__device__ __forceinline__ void ho_wait_heads(const Params &p, int ks, int lane, const unsigned *hb, int l) {
+  const int nh = p.pl.kc_oa / p.D, h0 = ks * nh;
+  for (int h = h0; h < h0 + nh; h++) ho_wait(p.sync, kHoAtt + h, hb[kHoAtt + h] + (unsigned)(l + 1) * (unsigned)p.M, lane);
+}
+
+// wo_a without the fold (more than 16 rows), with the hand-off waits
+template <int MAXG>
+__device__ __forceinline__ void st_wo_a_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
+                                           const unsigned *hb, int l) {
+  const int N = p.orr, K = p.H * p.D, kc = p.pl.kc_oa, ntile = N >> 4, T = ntile * (K / kc);
+  int t = cx.gw;
+  if (t >= T) return;
+  ho_wait_heads(p, t / ntile, cx.lane, hb, l);
+  linear_task<kW8T32, MAXG>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t, &pf, pf.on);
+  for (t += cx.nw; t < T; t += cx.nw) {
+    ho_wait_heads(p, t / ntile, cx.lane, hb, l);
+    linear_task<kW8T32, MAXG>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t);
+  }
+}
+
+// wq_b with the hand-offs: wait for every q row, then count each finished task for its head
+template <int MAXG, bool ONE>
+__device__ __forceinline__ void st_wq_b_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
+                                           const unsigned *hb, int l) {
+  const int N = p.H * p.D, K = p.qr, kc = p.pl.kc_qb, ntile = N >> 4, T = ntile * (K / kc);
+  int t = cx.gw;
+  if (t >= T) return;
+  const int c = bid() & 7;
+  ho_wait(p.sync, kHoQ + c, hb[kHoQ + c] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+  linear_task<kW8T32, MAXG>(t, cx.lane, w.wq_b, w.wq_b_s, nullptr, N, K, kc, p.s.qb, p.M, p.s.p_q, &pf, pf.on);
+  ho_count(p.sync, kHoQb + ((t % ntile) << 4) / p.D, cx.lane);
+  if constexpr (ONE) return;
+  for (t += cx.nw; t < T; t += cx.nw) {
+    linear_task<kW8T32, MAXG>(t, cx.lane, w.wq_b, w.wq_b_s, nullptr, N, K, kc, p.s.qb, p.M, p.s.p_q);
+    ho_count(p.sync, kHoQb + ((t % ntile) << 4) / p.D, cx.lane);
+  }
+}
+
 __device__ __forceinline__ void st_wo_a_fold(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
-                                             unsigned base) {
+                                             unsigned base, const unsigned *hb, int l) {
   const int N = p.orr, K = p.H * p.D, kc = p.pl.kc_oa, nks = K / kc, T = (N >> 4) * nks;
   const int t = cx.gw;
   if (t >= T) return;
+  if (p.ho) ho_wait_heads(p, t / (N >> 4), cx.lane, hb, l);
   linear_task<kW8T32, 1>(t, cx.lane, w.wo_a, w.wo_a_s, nullptr, N, K, kc, p.s.ob, p.M, p.s.p_t, &pf, pf.on);
   const int j = tq_group(p, cx);
   __builtin_amdgcn_s_waitcnt(0);  // this task's partials are at the coherence point
@@ -1368,7 +1430,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ unsigned tq_base[kWavesPerBlock];  // each wave's wo_a group counter before this layer
   __shared__ unsigned cb_base[kWavesPerBlock];  // each wave's combine group counter before this layer
   const unsigned nb = gridDim.x;
-  int mode, n_layers, a8;
+  __shared__ unsigned ho_base[kHoSlots];         // hand-off counters before this launch
+  int mode, n_layers, a8, ho;
   SyncWords *sw;
   Tracer tr;
   {
@@ -1376,12 +1439,17 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     mode = kp->mode;
     n_layers = kp->n_layers;
     a8 = kp->a8;
+    ho = kp->ho;
     sw = kp->sync;
     tr.buf = kp->trace;
   }
   // the barrier's thread reads the barrier base (the last wave has no work on the first
   // stage's critical path)
   if (tid() == kBarrierThread) bar_next = barrier_base(sw) + 1u;
+  // the hand-off counters' values before this launch, read before the block's first arrival:
+  // no producer of the launch counts before every block has arrived at the first barrier
+  if (ho && tid() < kHoSlots)
+    ho_base[tid()] = __hip_atomic_load(gptr(&sw->ho[tid()][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool moe_mode = mode == kModeMoe;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
@@ -1430,30 +1498,46 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         pa = linear_prefetch_addr<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb);
         st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0]);
       }
-      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
+      // With hand-offs ("Mono decode layer for DeepSeek-V4.1-Flash on MI355X", Design: the
+      // stages pass data between CTAs through tagged flags) no grid barrier separates
+      // qkv_post, wq_b, the attention and wo_a: each consumer waits on the counters of its
+      // own producers (every q row; its head's wq_b tasks and the step's records; its K
+      // chunk's heads), and the next weights are loaded as soon as a wave is free.
+      if (ho) {
+        linear_prefetch<kW8T32>(pa, pf_wq_b);
+      } else {
+        SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
+      }
       {
         STAGE(l);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb, p.M,
-                                               p.s.p_q, pf_wq_b);
+        if (ho)
+          st_wq_b_ho<NARROW ? 1 : 3, NARROW>(p, cx, w, pf_wq_b, ho_base, l);
+        else
+          linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb,
+                                                 p.M, p.s.p_q, pf_wq_b);
       }
-      SYNC();
+      if (!ho) SYNC();
       PreA pf_wo_a = pre_none();
       {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa);
         float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
         if constexpr (NARROW) {
-          st_attention_v<8>(p, cx, kv, lds);
+          st_attention_v<8>(p, cx, kv, lds, ho_base, l);
         } else {
           switch (p.D) {
-            case 64: st_attention_v<1>(p, cx, kv, lds); break;
-            case 128: st_attention_v<2>(p, cx, kv, lds); break;
-            case 256: st_attention_v<4>(p, cx, kv, lds); break;
-            default: st_attention_v<8>(p, cx, kv, lds); break;
+            case 64: st_attention_v<1>(p, cx, kv, lds, ho_base, l); break;
+            case 128: st_attention_v<2>(p, cx, kv, lds, ho_base, l); break;
+            case 256: st_attention_v<4>(p, cx, kv, lds, ho_base, l); break;
+            default: st_attention_v<8>(p, cx, kv, lds, ho_base, l); break;
           }
         }
       }
-      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
+      if (ho) {
+        linear_prefetch<kW8T32>(pa, pf_wo_a);
+      } else {
+        SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
+      }
       PreA pf_wo_b = pre_none();
       bool fold;
       {
@@ -1461,7 +1545,9 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         fold = NARROW || tq_fold(p);  // (the host picks the narrow kernel only where it holds)
         if (fold) {
           pa = linear_prefetch_addr<kW8T32>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob);
-          st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave]);
+          st_wo_a_fold(p, cx, w, pf_wo_a, tq_base[cx.wave], ho_base, l);
+        } else if (ho) {
+          st_wo_a_ho<NARROW ? 1 : 3>(p, cx, w, pf_wo_a, ho_base, l);
         } else {
           linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa, p.s.ob, p.M,
                                                  p.s.p_t, pf_wo_a);
@@ -1603,6 +1689,7 @@ struct dsl_layer {
   dsl_dims d{};
   int dev = 0, cus = 0, grid = 0, bpc = 0, S = 1;
   int last_kernel = -1;  // instantiation of the most recent launch: 1 narrow, 0 general
+  bool handoff = true;   // producer hand-offs where the launch allows them (DSL_HANDOFF=0: grid barriers)
   Plan plan{};
   dsl_weights *dw = nullptr;  // device copy of the weight descriptors
   SyncWords *sync = nullptr;
@@ -1841,6 +1928,10 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   L->plan.kc_sh13 = pick_kc(dims->hidden, 1024);
   L->plan.kc_shd = pick_kc(dims->shared_inter, 512);
   L->plan.kc_router = pick_kc(dims->hidden, 1024);
+  {
+    const char *e = getenv("DSL_HANDOFF");
+    L->handoff = !(e && e[0] == '0');
+  }
   if (hipMalloc((void **)&L->sync, sizeof(SyncWords)) != hipSuccess ||
       hipMalloc((void **)&L->dw, sizeof(dsl_weights) * dims->n_layers) != hipSuccess) {
     dsl_layer_destroy(L);
@@ -1923,6 +2014,9 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   p.eps = d.norm_eps; p.lim = d.swiglu_limit;
   p.attn_scale = 1.0f / sqrtf((float)d.head_dim);
   p.M = M; p.mode = mode; p.S = L->S; p.pl = L->plan;
+  // producer hand-offs around the attention: every row's post-processing on a block of its
+  // own (3 M blocks), heads within the counters, wo_a K chunks of whole heads
+  p.ho = mode != kModeMoe && L->grid >= 3 * M && d.n_heads <= kHoHeads && p.pl.kc_oa % d.head_dim == 0 && L->handoff;
   p.w = L->dw;
   if (kv)
     for (int l = 0; l < nl; l++) p.kv[l] = kv[l];

@@ -67,6 +67,7 @@ struct Params {
   int a8;  // the routed experts take MXFP8 activations (A8W4)
   float eps, lim, attn_scale;
   int M, mode, S;
+  int ho;  // the attention's producers hand off through counters instead of grid barriers
   Plan pl;
   const dsl_weights *w;  // device array [n_layers]
   dsl_kv kv[DSL_MAX_LAYERS];
