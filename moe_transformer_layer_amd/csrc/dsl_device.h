@@ -287,7 +287,7 @@ struct SyncWords {
   unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
   unsigned tq[64][16];      // wo_a tasks finished per 32-column group of t; only grow
   unsigned cb[128][16];     // down-stage waves finished per 32-column group of the MoE output; only grow
-  unsigned ho[80][64];      // producer hand-off counters (kHo* below); only grow
+  unsigned ho[136][64];     // producer hand-off counters (kHo* below); only grow
   unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };
@@ -295,10 +295,18 @@ struct SyncWords {
 enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 
 // Hand-off counters: finished producers of one consumer set, counted after each producer's
-// stores have drained.  kHoQ .. +7: q rows (one copy per group of blocks, so the pollers
-// spread over 8 lines); kHoKv: kv records and key-offset rows; kHoQb + h: wq_b tasks of head
-// h; kHoAtt + h: attention items of head h.
-enum : int { kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoSlots = 73, kHoHeads = 32 };
+// stores have drained.  A row counter has 8 copies that every row increments (its pollers
+// spread over 8 lines); a task counter has 8 copies of which task t increments copy t mod 8
+// (its increments spread over 8 lines) and its pollers sum them.
+//   kHoQ: q rows (qkv_post); kHoKv: kv records and key-offset rows (one counter);
+//   kHoQb + h: wq_b tasks of head h; kHoAtt + h: attention items of head h;
+//   kHoWq / kHoWkv: wqkv tasks of the q / kv latent columns (task counters);
+//   kHoTb + c: quantized t groups of wo_b's K chunk c; kHoWb: wo_b tasks (task counter);
+//   kHoU: MoE input rows; kHoRt / kHoSh: router and shared gate/up tasks (task counters).
+enum : int {
+  kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoWq = 73, kHoWkv = 81, kHoTb = 89, kHoWb = 97, kHoU = 105,
+  kHoRt = 113, kHoSh = 121, kHoSlots = 129, kHoHeads = 32, kHoTbChunks = 8
+};
 
 // Waits until counter id reaches target (modular, like the barrier's release word): lane 0
 // polls, the wave follows.  Bounded like the barrier's spin: a count that never arrives
@@ -315,6 +323,26 @@ __device__ __forceinline__ void ho_wait(SyncWords *sw, int id, unsigned target, 
     }
   }
   asm volatile("" ::: "memory");  // the consumer's loads stay after the wait
+}
+
+// The same for a task counter: waits until its 8 copies sum to target
+__device__ __forceinline__ void ho_wait_sum8(SyncWords *sw, int id, unsigned target, int lane) {
+  if (lane == 0) {
+    unsigned spins = 0;
+    for (;;) {
+      unsigned sum = 0;
+#pragma unroll
+      for (int c = 0; c < 8; c++)
+        sum += __hip_atomic_load(gptr(&sw->ho[id + c][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)(sum - target) >= 0) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1u << 24)) {
+        __hip_atomic_fetch_or(gptr(&sw->health), (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
 }
 
 // Counts one finished producer on counter id: the wave's stores are drained first, so the

@@ -104,6 +104,22 @@ __device__ __forceinline__ int64_t slot_of(const Params &p, const dsl_kv &kv, in
   return blk < 0 ? -1 : (int64_t)blk * p.B + (t - lb * p.B);
 }
 
+// Hand-off targets of layer l: each counter grows by a fixed number per layer, read relative
+// to its value at the start of the launch (hb, in LDS)
+__device__ __forceinline__ unsigned ho_per_qb(const Params &p) { return (unsigned)((p.D >> 4) * (p.qr / p.pl.kc_qb)); }
+__device__ __forceinline__ unsigned hb_sum8(const unsigned *hb, int id) {
+  unsigned s = 0;
+#pragma unroll
+  for (int c = 0; c < 8; c++) s += hb[id + c];
+  return s;
+}
+// tasks per layer of the task counters
+__device__ __forceinline__ int ho_t_wq(const Params &p) { return (p.qr >> 4) * (p.h / p.pl.kc_qkv); }
+__device__ __forceinline__ int ho_t_wkv(const Params &p) { return (p.D >> 4) * (p.h / p.pl.kc_qkv); }
+__device__ __forceinline__ int ho_t_wb(const Params &p) { return (p.h >> 4) * (p.orr / p.pl.kc_ob); }
+__device__ __forceinline__ int ho_t_rt(const Params &p) { return p.E * (p.h / p.pl.kc_router); }
+__device__ __forceinline__ int ho_t_sh(const Params &p) { return ((2 * p.Is) >> 4) * (p.h / p.pl.kc_sh13); }
+
 // q latent: sum the split-K partials, RMSNorm, MXFP8.
 template <int E>
 __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red) {
@@ -180,13 +196,23 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 // NARROW: the narrow-step kernel (q rank 1024, head dim 512: 2 and 1 elements per thread)
 template <bool NARROW>
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
-                                            uint8_t *tmp) {
+                                            uint8_t *tmp, const unsigned *hb, int l) {
   const int eq = NARROW ? 2 : row_elems(p.qr), ekv = NARROW ? 1 : row_elems(p.D);
   // q of row m on block m, kv of row m on block M + m, row m's key offsets on block 2 M + m
   // (with fewer than 3 M blocks the key offsets come from the norm stage, with fewer than
   // 2 M all of a row's work is block m's)
   if ((int)gridDim.x >= 2 * p.M) {
     const int b = bid();
+    if (p.ho >= 2 && b < 2 * p.M) {
+      // hand-off: every wqkv task of the row's part (q latent, or kv latent) has stored its partials
+      if (tid() == 0) {
+        if (b < p.M)
+          ho_wait_sum8(p.sync, kHoWq, hb_sum8(hb, kHoWq) + (unsigned)(l + 1) * (unsigned)ho_t_wq(p), 0);
+        else
+          ho_wait_sum8(p.sync, kHoWkv, hb_sum8(hb, kHoWkv) + (unsigned)(l + 1) * (unsigned)ho_t_wkv(p), 0);
+      }
+      __syncthreads();
+    }
     if (b >= 2 * p.M && b < 3 * p.M) key_offsets_row(p, kv, b - 2 * p.M);
     if (b < p.M) {
       switch (eq) {
@@ -346,10 +372,6 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
 // splits' partials meet in LDS (lds: 8 D + 16 floats), where one wave per item combines
 // them, quantizes the output to MXFP8 (a 32-block spans 32 / V lanes) and stores it.
 // Pad rows give zeros.
-// Hand-off targets of layer l: each counter grows by a fixed number per layer, read relative
-// to its value at the start of the launch (hb, in LDS)
-__device__ __forceinline__ unsigned ho_per_qb(const Params &p) { return (unsigned)((p.D >> 4) * (p.qr / p.pl.kc_qb)); }
-
 template <int V>
 __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds,
                                                const unsigned *hb, int l) {
@@ -522,15 +544,57 @@ __device__ __forceinline__ void st_wo_a_fold(const Params &p, const Ctx &cx, con
   if (old - base != 2u * (unsigned)nks - 1u) return;
   asm volatile("" ::: "memory");  // the partial loads stay after the count
   tq_group_quant(p, j, cx.lane);
+  if (p.ho >= 2) ho_count(p.sync, kHoTb + (32 * j) / p.pl.kc_ob, cx.lane);
+}
+
+// wqkv with the hand-offs: count each finished task for its part (q or kv latent columns)
+template <int MAXG, bool ONE>
+__device__ __forceinline__ void st_wqkv_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf) {
+  const int N = p.qr + p.D, K = p.h, kc = p.pl.kc_qkv, ntile = N >> 4, T = ntile * (K / kc);
+  int t = cx.gw;
+  if (t >= T) return;
+  linear_task<kW8T32, MAXG>(t, cx.lane, w.wqkv, w.wqkv_s, nullptr, N, K, kc, p.s.xb, p.M, p.s.p_qkv, &pf, pf.on);
+  ho_count(p.sync, (((t % ntile) << 4) < p.qr ? kHoWq : kHoWkv) + (t & 7), cx.lane);
+  if constexpr (ONE) return;
+  for (t += cx.nw; t < T; t += cx.nw) {
+    linear_task<kW8T32, MAXG>(t, cx.lane, w.wqkv, w.wqkv_s, nullptr, N, K, kc, p.s.xb, p.M, p.s.p_qkv);
+    ho_count(p.sync, (((t % ntile) << 4) < p.qr ? kHoWq : kHoWkv) + (t & 7), cx.lane);
+  }
+}
+
+// wo_b with the hand-offs: each task waits for its K chunk's t groups (when wo_a's output
+// quantization is folded in) and is counted when done
+template <int MAXG, bool ONE>
+__device__ __forceinline__ void st_wo_b_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
+                                           const unsigned *hb, int l, bool wait_tb) {
+  const int N = p.h, K = p.orr, kc = p.pl.kc_ob, ntile = N >> 4, T = ntile * (K / kc);
+  const unsigned groups = (unsigned)(kc >> 5);
+  int t = cx.gw;
+  if (t >= T) return;
+  if (wait_tb) ho_wait(p.sync, kHoTb + t / ntile, hb[kHoTb + t / ntile] + (unsigned)(l + 1) * groups, cx.lane);
+  linear_task<kW8T32, MAXG>(t, cx.lane, w.wo_b, w.wo_b_s, nullptr, N, K, kc, p.s.tb, p.M, p.s.p_a, &pf, pf.on);
+  ho_count(p.sync, kHoWb + (t & 7), cx.lane);
+  if constexpr (ONE) return;
+  for (t += cx.nw; t < T; t += cx.nw) {
+    if (wait_tb) ho_wait(p.sync, kHoTb + t / ntile, hb[kHoTb + t / ntile] + (unsigned)(l + 1) * groups, cx.lane);
+    linear_task<kW8T32, MAXG>(t, cx.lane, w.wo_b, w.wo_b_s, nullptr, N, K, kc, p.s.tb, p.M, p.s.p_a);
+    ho_count(p.sync, kHoWb + (t & 7), cx.lane);
+  }
 }
 
 // wo_b output a (sum of partials).  Attention-only steps write bf16(a).  Full steps:
 // hres = bf16(x + a), u = bf16(RMSNorm_ffn(hres)).  Pad rows give zeros.
 template <int E>
-__device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, bool last, float *red) {
+__device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights &w, const uint16_t *xin, bool last, float *red,
+                                              const unsigned *hb, int l) {
   const int h = p.h, nks = p.orr / p.pl.kc_ob, k = tid() * E;
   const bool act = k < h;
   for (int m = bid(); m < p.M; m += gridDim.x) {
+    if (p.ho >= 2) {
+      // hand-off: every wo_b task of the layer has stored its partials
+      if (tid() == 0) ho_wait_sum8(p.sync, kHoWb, hb_sum8(hb, kHoWb) + (unsigned)(l + 1) * (unsigned)ho_t_wb(p), 0);
+      __syncthreads();
+    }
     const bool live = ldg(p.pos + m) >= 0;
     float a[E], hr[E], gm[E];
     if (act) {
@@ -549,22 +613,30 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
     const size_t off = (size_t)m * h + k;
     if (p.mode == kModeAttn) {
       if (act) store_bf16<E>(p.out + off, a);
-      continue;
+      continue;  // (block-uniform)
     }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; e++) ss += hr[e] * hr[e];
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)h + p.eps);
-    if (!act) continue;
-    store_bf16<E>(p.s.hres + off, hr);
-    if (last && p.taps.hres) store_bf16<E>((uint16_t *)p.taps.hres + off, hr);
-    if (last && p.taps.attn_out) store_bf16<E>((uint16_t *)p.taps.attn_out + off, a);
-    float uu[E];
+    if (act) {
+      store_bf16<E>(p.s.hres + off, hr);
+      if (last && p.taps.hres) store_bf16<E>((uint16_t *)p.taps.hres + off, hr);
+      if (last && p.taps.attn_out) store_bf16<E>((uint16_t *)p.taps.attn_out + off, a);
+      float uu[E];
 #pragma unroll
-    for (int e = 0; e < E; e++) uu[e] = live ? hr[e] * r * gm[e] : 0.f;
-    store_bf16<E>(p.s.u + off, uu);
-    if (last && p.taps.moe_in) store_bf16<E>((uint16_t *)p.taps.moe_in + off, uu);
+      for (int e = 0; e < E; e++) uu[e] = live ? hr[e] * r * gm[e] : 0.f;
+      store_bf16<E>(p.s.u + off, uu);
+      if (last && p.taps.moe_in) store_bf16<E>((uint16_t *)p.taps.moe_in + off, uu);
+    }
+    if (p.ho >= 2) {
+      // hand-off: the row's u is out; one count on each copy of the row counter
+      barrier_drain();
+      __syncthreads();
+      if (tid() < 8)
+        __hip_atomic_fetch_add(gptr(&p.sync->ho[kHoU + tid()][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -652,11 +724,17 @@ __device__ __forceinline__ void router_task_j(const Params &p, const float *__re
 // Router partial logits ((expert, K chunk) tasks) and the shared expert's gate/up
 // partials, together: both read only the MoE input.
 template <bool NARROW>
-__device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u) {
+__device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx, const dsl_weights &w, const uint16_t *u,
+                                                 const unsigned *hb, int l) {
   const int TR = p.E * (p.h / p.pl.kc_router);
   const int Nsh = 2 * p.Is;
   const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
   const int J = (p.pl.kc_router + 511) >> 9;
+  if (p.ho >= 2) {
+    // hand-off: every row's u is out
+    const int c = bid() & 7;
+    ho_wait(p.sync, kHoU + c, hb[kHoU + c] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+  }
   // (narrow: at most one task per wave, which the host checks)
   for (int t = cx.gw; t < TR + TS; t += NARROW ? 1 << 30 : cx.nw) {
     if (t < TR) {
@@ -665,9 +743,11 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
         router_task_j<1>(p, w.w_router, u, e, c, cx.lane);
       else
         router_task_j<2>(p, w.w_router, u, e, c, cx.lane);
+      if (p.ho >= 2) ho_count(p.sync, kHoRt + (t & 7), cx.lane);
     } else {
       linear_task<kW8B128, NARROW ? 1 : 3>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u,
                                            p.M, p.s.p_sh);
+      if (p.ho >= 2) ho_count(p.sync, kHoSh + ((t - TR) & 7), cx.lane);
     }
   }
   if (p.a8) st_u_quant(p, cx, u);
@@ -833,10 +913,12 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
 }
 
 // Shared SwiGLU over all (row, column): z = bf16(swiglu_clamp(gate, up))
-__device__ __forceinline__ void st_shared_swiglu(const Params &p, bool all_live) {
+__device__ __forceinline__ void st_shared_swiglu(const Params &p, bool all_live, bool wait, const unsigned *hb, int l) {
   const int Is = p.Is, nks = p.h / p.pl.kc_sh13;
   const size_t pstride = (size_t)p.M * 2 * Is;
   const int total = p.M * Is;
+  if (wait && bid() * kThreads + (tid() & ~63) < total)
+    ho_wait_sum8(p.sync, kHoSh, hb_sum8(hb, kHoSh) + (unsigned)(l + 1) * (unsigned)ho_t_sh(p), tid() & 63);
   for (int idx = bid() * kThreads + tid(); idx < total; idx += gridDim.x * kThreads) {
     const int m = idx / Is, n = idx - m * Is;
     float z = 0.f;
@@ -1431,7 +1513,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ unsigned cb_base[kWavesPerBlock];  // each wave's combine group counter before this layer
   const unsigned nb = gridDim.x;
   __shared__ unsigned ho_base[kHoSlots];         // hand-off counters before this launch
-  int mode, n_layers, a8, ho;
+  int mode, n_layers, a8, ho, Mrows;
   SyncWords *sw;
   Tracer tr;
   {
@@ -1440,6 +1522,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     n_layers = kp->n_layers;
     a8 = kp->a8;
     ho = kp->ho;
+    Mrows = kp->M;
     sw = kp->sync;
     tr.buf = kp->trace;
   }
@@ -1451,6 +1534,9 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   if (ho && tid() < kHoSlots)
     ho_base[tid()] = __hip_atomic_load(gptr(&sw->ho[tid()][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool moe_mode = mode == kModeMoe;
+  // full hand-offs (ho >= 2) also replace the barriers after wqkv, wo_b, the FFN norm and
+  // (steps whose top-k runs in every block, bf16 expert inputs) the router
+  const bool ho2 = ho >= 2, ho_router = ho2 && Mrows <= kTopkInBlockRows && !a8;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
     const bool last = l == n_layers - 1;
@@ -1488,15 +1574,18 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
       {
         STAGE(l);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb, p.M,
-                                               p.s.p_qkv, pf_wqkv);
+        if (ho2)
+          st_wqkv_ho<NARROW ? 1 : 3, NARROW>(p, cx, w, pf_wqkv);
+        else
+          linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb,
+                                                 p.M, p.s.p_qkv, pf_wqkv);
       }
-      SYNC();
+      if (!ho2) SYNC();
       PreA pf_wq_b = pre_none();
       {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb);
-        st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0]);
+        st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0], ho_base, l);
       }
       // With hand-offs ("Mono decode layer for DeepSeek-V4.1-Flash on MI355X", Design: the
       // stages pass data between CTAs through tagged flags) no grid barrier separates
@@ -1571,27 +1660,34 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           }
         }
       }
-      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_b));
+      if (ho2 && fold) {
+        linear_prefetch<kW8T32>(pa, pf_wo_b);
+      } else {
+        SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_b));
+      }
       {
         STAGE(l);
-        // (this wave's own slot, read in wo_a before the barrier)
+        // (this wave's own slot, read in wo_a)
         if (fold && cx.lane == 0) tq_base[cx.wave] += 2u * (unsigned)((p.H * p.D) / p.pl.kc_oa);
-        linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M, p.s.p_a,
-                                               pf_wo_b);
+        if (ho2)
+          st_wo_b_ho<NARROW ? 1 : 3, NARROW>(p, cx, w, pf_wo_b, ho_base, l, fold);
+        else
+          linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M,
+                                                 p.s.p_a, pf_wo_b);
       }
-      SYNC();
+      if (!ho2) SYNC();
       {
         STAGE(l);
         const uint16_t *xin = A_.xin;
         if constexpr (NARROW) {
-          st_ffn_norm_e<8>(p, w, xin, last, red);
+          st_ffn_norm_e<8>(p, w, xin, last, red, ho_base, l);
         } else {
           switch (row_elems(p.h)) {
-            case 1: st_ffn_norm_e<1>(p, w, xin, last, red); break;
-            case 2: st_ffn_norm_e<2>(p, w, xin, last, red); break;
-            case 4: st_ffn_norm_e<4>(p, w, xin, last, red); break;
-            case 8: st_ffn_norm_e<8>(p, w, xin, last, red); break;
-            default: st_ffn_norm_e<16>(p, w, xin, last, red); break;
+            case 1: st_ffn_norm_e<1>(p, w, xin, last, red, ho_base, l); break;
+            case 2: st_ffn_norm_e<2>(p, w, xin, last, red, ho_base, l); break;
+            case 4: st_ffn_norm_e<4>(p, w, xin, last, red, ho_base, l); break;
+            case 8: st_ffn_norm_e<8>(p, w, xin, last, red, ho_base, l); break;
+            default: st_ffn_norm_e<16>(p, w, xin, last, red, ho_base, l); break;
           }
         }
       }
@@ -1599,20 +1695,23 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         tr.mark();
         return;
       }
-      SYNC();
+      if (!ho2) SYNC();
     }
     {
       STAGE(l);
       // (a MoE step's first stage: before this block's first arrival)
       if (moe_mode && l == 0 && cx.lane == 0) cb_base[cx.wave] = cb_read_base(p, cx);
-      st_router_shared<NARROW>(p, cx, w, moe_mode ? p.x : p.s.u);
+      st_router_shared<NARROW>(p, cx, w, moe_mode ? p.x : p.s.u, ho_base, l);
     }
-    SYNC();
+    if (!ho_router) SYNC();
     {
       STAGE(l);
       if (NARROW || p.M <= kTopkInBlockRows) {
         // no grid barrier between the router and the experts: every block selects the
-        // experts of every row itself
+        // experts of every row itself (with hand-offs, once every router task has stored
+        // its partial logits)
+        if (ho_router && cx.wave < p.M)
+          ho_wait_sum8(p.sync, kHoRt, hb_sum8(ho_base, kHoRt) + (unsigned)(l + 1) * (unsigned)ho_t_rt(p), cx.lane);
         topk_in_block(p, cx, R, moe_mode, last && bid() == 0 ? p.taps.logits : nullptr);
         tr.mark();
         tr.mark();
@@ -1638,7 +1737,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       st_routed_gate_up<NARROW>(p, cx, w, R, p.a8 ? p.s.uq : moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
       // the shared SwiGLU, off the critical path: its reader, the shared down projection,
       // comes after the next grid barrier
-      st_shared_swiglu(p, moe_mode);
+      st_shared_swiglu(p, moe_mode, ho_router, ho_base, l);
     }
     SYNC();
     if (a8) {
@@ -1689,7 +1788,8 @@ struct dsl_layer {
   dsl_dims d{};
   int dev = 0, cus = 0, grid = 0, bpc = 0, S = 1;
   int last_kernel = -1;  // instantiation of the most recent launch: 1 narrow, 0 general
-  bool handoff = true;   // producer hand-offs where the launch allows them (DSL_HANDOFF=0: grid barriers)
+  int handoff = 2;       // producer hand-offs where the launch allows them: 2 all, 1 around the
+                         // attention only, 0 none (grid barriers); DSL_HANDOFF overrides
   Plan plan{};
   dsl_weights *dw = nullptr;  // device copy of the weight descriptors
   SyncWords *sync = nullptr;
@@ -1930,7 +2030,7 @@ int dsl_layer_build(const dsl_dims *dims, const dsl_weights *weights, dsl_layer 
   L->plan.kc_router = pick_kc(dims->hidden, 1024);
   {
     const char *e = getenv("DSL_HANDOFF");
-    L->handoff = !(e && e[0] == '0');
+    if (e && e[0] >= '0' && e[0] <= '2') L->handoff = e[0] - '0';
   }
   if (hipMalloc((void **)&L->sync, sizeof(SyncWords)) != hipSuccess ||
       hipMalloc((void **)&L->dw, sizeof(dsl_weights) * dims->n_layers) != hipSuccess) {
@@ -2016,7 +2116,10 @@ static int launch(dsl_layer *L, int mode, const void *x, int M, const dsl_kv *kv
   p.M = M; p.mode = mode; p.S = L->S; p.pl = L->plan;
   // producer hand-offs around the attention: every row's post-processing on a block of its
   // own (3 M blocks), heads within the counters, wo_a K chunks of whole heads
-  p.ho = mode != kModeMoe && L->grid >= 3 * M && d.n_heads <= kHoHeads && p.pl.kc_oa % d.head_dim == 0 && L->handoff;
+  // (level 2 also needs wo_b's K chunks within the counters)
+  p.ho = mode != kModeMoe && L->grid >= 3 * M && d.n_heads <= kHoHeads && p.pl.kc_oa % d.head_dim == 0
+             ? (L->handoff >= 2 && d.o_rank / p.pl.kc_ob <= kHoTbChunks ? 2 : L->handoff)
+             : 0;
   p.w = L->dw;
   if (kv)
     for (int l = 0; l < nl; l++) p.kv[l] = kv[l];
