@@ -23,8 +23,8 @@
  *     the cache) is reported by dsl_layer_health().
  *   - The caller owns x, out, the weights, the KV caches and the tables; the
  *     handle owns its sync buffer and one scratch buffer per step width.  The
- *     weights are read in place, never copied ("Design": weights are read in
- *     place with no second copy).  A handle is not thread-safe, and two steps of
+ *     kernels stream the caller's weight buffers directly and keep no copy of
+ *     them (PR 60397, Design).  A handle is not thread-safe, and two steps of
  *     one handle must not run concurrently on different streams.
  *   - Step widths M are 1..dims.max_rows (max_rows <= 48: "Scope", decode only,
  *     at most 48 rows).  Each width gets its own scratch at its first step
@@ -37,8 +37,9 @@
  *     (2^24 polls of the release word, each a device-memory round trip) makes the
  *     step report DSL_EDEVICE instead of hanging.
  *   - positions[r] = -1 marks a pad row: no KV write, ids -1, weights 0 and zero
- *     rows in every output ("Test Plan": the kernels skip pad rows, whose slot
- *     is -1).  Rows of one request must have distinct positions.
+ *     rows in every output (PR 60397, Test Plan: padded steps mark their unused
+ *     rows with slot -1 and the kernels leave them out).  Rows of one request must
+ *     have distinct positions.
  */
 #ifndef DSL_H
 #define DSL_H

@@ -1492,6 +1492,17 @@ constexpr unsigned kBarrierThread = kThreads - kWave;
     tr.mark();                \
   } while (0)
 #define SYNC() SYNC_PF((void)0)
+// A grid barrier, or (where hand-offs replace it) the trace's two stamps only, so that the
+// stamps keep their numbering either way
+#define SYNC_IF(C)      \
+  do {                  \
+    if (C) {            \
+      SYNC();           \
+    } else {            \
+      tr.mark();        \
+      tr.mark();        \
+    }                   \
+  } while (0)
 
 #define STAGE(l) const StageArgs A_ = stage_args(l); const Params &p = A_.p; const dsl_weights &w = A_.w; \
   const dsl_kv &kv = A_.kv; const Ctx cx = make_ctx(); (void)p; (void)w; (void)kv; (void)cx
@@ -1580,7 +1591,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb,
                                                  p.M, p.s.p_qkv, pf_wqkv);
       }
-      if (!ho2) SYNC();
+      SYNC_IF(!ho2);
       PreA pf_wq_b = pre_none();
       {
         STAGE(l);
@@ -1594,6 +1605,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       // chunk's heads), and the next weights are loaded as soon as a wave is free.
       if (ho) {
         linear_prefetch<kW8T32>(pa, pf_wq_b);
+        tr.mark();
+        tr.mark();
       } else {
         SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wq_b));
       }
@@ -1605,7 +1618,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb, p.s.qb,
                                                  p.M, p.s.p_q, pf_wq_b);
       }
-      if (!ho) SYNC();
+      SYNC_IF(!ho);
       PreA pf_wo_a = pre_none();
       {
         STAGE(l);
@@ -1624,6 +1637,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       }
       if (ho) {
         linear_prefetch<kW8T32>(pa, pf_wo_a);
+        tr.mark();
+        tr.mark();
       } else {
         SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_a));
       }
@@ -1662,6 +1677,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       }
       if (ho2 && fold) {
         linear_prefetch<kW8T32>(pa, pf_wo_b);
+        tr.mark();
+        tr.mark();
       } else {
         SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wo_b));
       }
@@ -1675,7 +1692,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
           linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wo_b, w.wo_b_s, nullptr, p.h, p.orr, p.pl.kc_ob, p.s.tb, p.M,
                                                  p.s.p_a, pf_wo_b);
       }
-      if (!ho2) SYNC();
+      SYNC_IF(!ho2);
       {
         STAGE(l);
         const uint16_t *xin = A_.xin;
@@ -1695,7 +1712,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         tr.mark();
         return;
       }
-      if (!ho2) SYNC();
+      SYNC_IF(!ho2);
     }
     {
       STAGE(l);
@@ -1703,7 +1720,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       if (moe_mode && l == 0 && cx.lane == 0) cb_base[cx.wave] = cb_read_base(p, cx);
       st_router_shared<NARROW>(p, cx, w, moe_mode ? p.x : p.s.u, ho_base, l);
     }
-    if (!ho_router) SYNC();
+    SYNC_IF(!ho_router);
     {
       STAGE(l);
       if (NARROW || p.M <= kTopkInBlockRows) {
@@ -1770,6 +1787,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
 
 #undef STAGE
 #undef SYNC
+#undef SYNC_IF
 
 }  // namespace dsl
 
