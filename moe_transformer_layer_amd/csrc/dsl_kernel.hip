@@ -1189,21 +1189,8 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   }
 }
 
-// A wave's task in a round after the first of a stage of T tasks, the round starting at task
-// `base`. When that round keeps more than half of the waves busy, its blocks are taken even
-// blocks first. Block b runs on XCD b mod 8, and the odd XCDs finish the expert stages a few
-// microseconds after the even ones, so the round's idle waves go to them. A shorter round keeps
-// the plain order and stays spread over every XCD. For an even grid this is a permutation of
-// the round's waves, so every task still goes to exactly one wave.
-__device__ __forceinline__ int later_round_task(const Ctx &cx, int base, int T) {
-  const int G = (int)gridDim.x;
-  if ((G & 1) || T - base <= (cx.nw >> 1)) return base + cx.gw;
-  const int b = bid();
-  return base + cx.wave * G + ((b & 1) ? (G >> 1) + (b >> 1) : (b >> 1));
-}
-
 // Routed gate/up tasks (selected expert, 16-row tile of gate and of up): task t to wave t mod
-// waves in the first round, then in the order later_round_task gives.
+// waves.
 // NARROW: hidden 4096 and at most 8 rows (one 16-row group).
 template <bool NARROW>
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
@@ -1211,7 +1198,7 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
   const int tiles_n = p.I >> 4;
   const int T = R.nd * tiles_n;
   const int qv = NARROW ? 2 : p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
-  for (int t = cx.gw, base = 0; t < T; base += cx.nw, t = later_round_task(cx, base, T)) {
+  for (int t = cx.gw; t < T; t += cx.nw) {
     // wave-uniform: keep them (and the addresses built on them) in scalar registers
     const int tu = __builtin_amdgcn_readfirstlane(t);
     const int q = tu / tiles_n, tile = tu - q * tiles_n;
