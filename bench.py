@@ -290,6 +290,7 @@ def main():
     ap.add_argument("--only-m6", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--only-m48", action="store_true", help="only the M=48 layer (for counter passes)")
+    ap.add_argument("--only-draft", action="store_true", help="only the three chained draft layers at M=6")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
@@ -307,6 +308,12 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     print("[bench] drawing the layer's weights", flush=True)
     weights = synth.make_weights("layer48", 7)
+    if args.only_draft:
+        draft = run_point(dsl, torch, "draft", 6, 2, args.steps, args.warmup, weights * 3,
+                          graph_replay=not args.no_graph)
+        print(f"[bench] draft M=6: {draft['us_per_layer_kernel']:.1f} us/layer, {draft['gbs']:.0f} GB/s", flush=True)
+        print(json.dumps({"draft_m6": draft}), flush=True)
+        return
     if args.only_m48:
         m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
                         graph_replay=not args.no_graph)
