@@ -11,7 +11,8 @@ from its own expert ids.
 
 Prints one JSON line: the M=6 full layer (top-6 of 128 experts) as the headline,
 the M=48 layer, the three chained draft layers at M=6 (top-3, per layer) and the
-layer with A8W4 experts (MXFP8 activations) at M=6 and M=48 as further points, the roofline of the launch (algorithmic HBM bytes per step over the
+layer with A8W4 experts (MXFP8 activations) at M=6 and M=48 and the draft head's skinny
+MXFP8 linear as further points, the roofline of the launch (algorithmic HBM bytes per step over the
 measured kernel time against 8 TB/s, and against a plain device copy's measured
 rate), the M=6 layer with warm weights (one copy; labelled, not the headline), and the
 CPU oracle timed on a bounded sample.  Each point also gives the wall
@@ -174,6 +175,46 @@ def run_point(dsl, torch, name: str, M: int, layers_dev: int, steps: int, warmup
                 us_per_layer_kernel=mean_us / nl, us_kernel_p10=per[len(per) // 10],
                 us_kernel_p50=per[len(per) // 2], us_kernel_p90=per[(9 * len(per)) // 10], gbs=gbs,
                 frac=gbs / PEAK_GBS, bytes=bsum, grid=grid, n_weight_copies=len(handles))
+
+
+def run_head(dsl, torch, steps: int, warmup: int, M: int = 6, N: int = 32320, K: int = 4096, copies: int = 4):
+    """The skinny MXFP8 linear at the draft head's reading (6 rows, N = 32320 = a 129280-row
+    vocabulary over four ranks, K = 4096), weights cold (copies rotated, 4 x 133 MB beyond the
+    256 MB Infinity Cache): microseconds per GEMM from HIP events on the launch stream, and the
+    algorithmic bytes (weights, scales, rows in, float32 out) over that time."""
+    import numpy as np
+
+    from moe_transformer_layer_amd import synth
+    rng = np.random.default_rng(21)
+    w, ws = synth.gen_mxfp8_weight(N, K, 1.5 / np.sqrt(K), rng)
+    x = torch.from_numpy(synth.gen_x(synth.CONFIGS["mid"].replace(hidden=K), rng, M).view("int16")).cuda()
+    wd = [torch.from_numpy(w).cuda() for _ in range(copies)]
+    sd = [torch.from_numpy(ws).cuda() for _ in range(copies)]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    wsb = dsl.dsl_linear_workspace_bytes(M, N, K)
+    buf = torch.empty(wsb + 256, dtype=torch.uint8, device="cuda")
+    base = (buf.data_ptr() + 255) & ~255
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        dsl.dsl_linear_mxfp8(x.data_ptr(), M, K, wd[i % copies].data_ptr(), sd[i % copies].data_ptr(), N, y.data_ptr(),
+                             base, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = N * K + (N // 32) * (K // 32) + M * K * 2 + M * N * 4
+    del wd, sd
+    torch.cuda.empty_cache()
+    return dict(M=M, N=N, K=K, us_per_gemm=us, bytes=byts, gbs=byts / (us * 1e-6) / 1e9,
+                frac=byts / (us * 1e-6) / 1e9 / PEAK_GBS, workspace_bytes=wsb, n_weight_copies=copies)
 
 
 def copy_gbs(torch, mib: int = 1024, reps: int = 10) -> float:
@@ -348,6 +389,11 @@ def main():
                            graph_replay=False)
         print(f"[bench] A8W4 M=6: {m6_a8['us_kernel_mean']:.1f} us/launch; M=48: {m48_a8['us_kernel_mean']:.1f} "
               f"us/launch", flush=True)
+    head = None
+    if not args.only_m6:
+        print("[bench] draft head GEMM (skinny MXFP8 linear, 6 x 4096 -> 32320)", flush=True)
+        head = run_head(dsl, torch, args.steps, args.warmup)
+        print(f"[bench] head GEMM: {head['us_per_gemm']:.1f} us, {head['gbs']:.0f} GB/s", flush=True)
     warm = None
     if not args.only_m6:
         # one weight copy for every launch: what stays in the 256 MB Infinity Cache between
@@ -387,6 +433,7 @@ def main():
         "draft_m6": draft,
         "a8w4_m6": m6_a8,
         "a8w4_m48": m48_a8,
+        "head_gemm_m6": head,
         "warm_m6": warm,
         "cpu_baseline": cpu,
     }

@@ -198,6 +198,29 @@ int dsl_attn_step(dsl_layer *layer, const void *x_bf16, int32_t M, const dsl_kv 
 int dsl_moe_step(dsl_layer *layer, const void *u_bf16, int32_t M, void *moe_out_bf16,
                  int32_t *topk_ids, float *topk_w, void *hip_stream);
 
+/* A skinny MXFP8 linear, y = MXq(x) . W^T, with float32 accumulation and output: the draft
+ * step's head GEMMs ("Mono decode for the DSpark draft layers", vLLM PR 62131, Details, where
+ * they are the step's largest cost after its layers), read here in the format and numerics of
+ * the layer's other dense linears (PR 60397, Design).  No handle: the call is stateless.
+ *   x    bf16 [M][K] device rows, 16-byte aligned; 1 <= M <= 48, K a multiple of 128.
+ *        Each 1x32 block along K is MXFP8-quantized (OCP MX: block exponent from the
+ *        float32 amax, e4m3 elements rounded to nearest even and saturated) before the
+ *        product, as for the layer's attention linears.
+ *   w    e4m3 row-major [N][K], 16-byte aligned; w_s one E8M0 per 32x32 tile [N/32][K/32];
+ *        N a multiple of 32.  Read in place.
+ *   y    float32 [M][N], 16-byte aligned, written whole.
+ *   workspace  device memory of dsl_linear_workspace_bytes(M, N, K) bytes, 256-byte
+ *        aligned, owned by the caller; overwritten (the quantized rows, and float32 split-K
+ *        partials when N / 16 output tiles alone would not fill the grid).
+ * Asynchronous on hip_stream (three launches).  Errors: DSL_EUNSUPPORTED for sizes outside
+ * the above, DSL_EINVAL for NULL or misaligned pointers, DSL_EHIP for a failed launch. */
+int dsl_linear_mxfp8(const void *x_bf16, int32_t M, int32_t K, const uint8_t *w, const uint8_t *w_s, int32_t N,
+                     float *y, void *workspace, void *hip_stream);
+
+/* Bytes of workspace dsl_linear_mxfp8 needs for these sizes, or -1 (with dsl_last_error) for
+ * sizes it does not take. */
+int64_t dsl_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
 /* Synchronizes nothing; reads the device health word after the caller has
  * synchronized.  0 = healthy; DSL_EDEVICE after a recorded device fault (the word
  * is then cleared and the handle's sync state reset). */

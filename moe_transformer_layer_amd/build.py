@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "dsl_kernel.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("dsl_kernel.hip", "dsl_linear.hip")]
 LIB = os.path.join(PKG, "libdsl.so")
 
 HIPCC_FLAGS = [
@@ -26,7 +26,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = True) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1816,6 +1816,12 @@ static int fail(int code, const char *fmt, ...) {
   return code;
 }
 
+// The same for the library's other sources (dsl_linear.hip)
+int dsl::set_error(int code, const char *msg) {
+  g_err = msg;
+  return code;
+}
+
 #define HIPCHK(call)                                                                          \
   do {                                                                                        \
     hipError_t e_ = (call);                                                                   \

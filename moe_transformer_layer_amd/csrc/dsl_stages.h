@@ -24,6 +24,9 @@
 
 namespace dsl {
 
+// Records the message dsl_last_error() returns and gives back code (host side).
+int set_error(int code, const char *msg);
+
 constexpr int kThreads = 512;
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kSplitKeys = 32;  // keys per attention split

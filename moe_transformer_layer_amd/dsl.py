@@ -76,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.dsl_layer_health.argtypes = [c_void_p]
         L.dsl_layer_grid.argtypes = [c_void_p, P(c_int32), P(c_int32)]
         L.dsl_layer_last_kernel.argtypes = [c_void_p]
+        L.dsl_linear_mxfp8.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                       c_void_p]
+        L.dsl_linear_mxfp8.restype = c_int32
+        L.dsl_linear_workspace_bytes.argtypes = [c_int32, c_int32, c_int32]
+        L.dsl_linear_workspace_bytes.restype = c_int64
         L.dsl_layer_set_trace.argtypes = [c_void_p, c_int32]
         L.dsl_layer_read_trace.argtypes = [c_void_p, ctypes.POINTER(ctypes.c_double), c_int32]
         L.dsl_layer_destroy.argtypes = [c_void_p]
@@ -153,6 +158,41 @@ def dsl_layer_last_kernel(h) -> int:
     if rc < -1:
         _check(rc)
     return rc
+
+
+def dsl_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    n = lib().dsl_linear_workspace_bytes(M, N, K)
+    if n < 0:
+        raise DslError(DSL_EUNSUPPORTED, lib().dsl_last_error().decode())
+    return n
+
+
+def dsl_linear_mxfp8(x: int, M: int, K: int, w: int, w_s: int, N: int, y: int, workspace: int, stream: int = 0):
+    _check(lib().dsl_linear_mxfp8(x, M, K, w, w_s, N, y, workspace, stream))
+
+
+class LinearOnDevice:
+    """One MXFP8 weight [N][K] (codes and E8M0 tiles) in device memory, run on bf16 rows."""
+
+    def __init__(self, w: np.ndarray, w_s: np.ndarray, device="cuda:0"):
+        import torch
+        self.torch = torch
+        self.dev = torch.device(device)
+        self.N, self.K = w.shape
+        self.w = torch.from_numpy(np.ascontiguousarray(w)).to(self.dev)
+        self.w_s = torch.from_numpy(np.ascontiguousarray(w_s)).to(self.dev)
+
+    def __call__(self, x_bits: np.ndarray) -> np.ndarray:
+        torch = self.torch
+        M = x_bits.shape[0]
+        x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(self.dev)
+        y = torch.empty((M, self.N), dtype=torch.float32, device=self.dev)
+        ws = torch.empty(dsl_linear_workspace_bytes(M, self.N, self.K) + 256, dtype=torch.uint8, device=self.dev)
+        base = (ws.data_ptr() + 255) & ~255
+        dsl_linear_mxfp8(x.data_ptr(), M, self.K, self.w.data_ptr(), self.w_s.data_ptr(), self.N, y.data_ptr(), base,
+                         torch.cuda.current_stream(self.dev).cuda_stream)
+        torch.cuda.synchronize(self.dev)
+        return y.cpu().numpy()
 
 
 def dsl_layer_set_trace(h, on: bool):

@@ -95,3 +95,27 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsl, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         dsl.lib()
+
+
+def test_linear_refuses_bad_arguments_on_the_host(lib):
+    """The skinny linear checks its sizes and pointers before any device call."""
+    assert dsl.dsl_linear_workspace_bytes(6, 4096, 4096) >= 6 * 4096 * 2
+    for M, N, K in ((0, 64, 128), (49, 64, 128), (6, 48, 128), (6, 64, 100)):
+        with pytest.raises(dsl.DslError) as ei:
+            dsl.dsl_linear_workspace_bytes(M, N, K)
+        assert ei.value.code == dsl.DSL_EUNSUPPORTED
+        rc = lib.dsl_linear_mxfp8(16, M, K, 16, 16, N, 16, 256, None)
+        assert rc == dsl.DSL_EUNSUPPORTED, (M, N, K)
+    assert lib.dsl_linear_mxfp8(None, 6, 128, 16, 16, 64, 16, 256, None) == dsl.DSL_EINVAL
+    assert lib.dsl_linear_mxfp8(8, 6, 128, 16, 16, 64, 16, 256, None) == dsl.DSL_EINVAL  # misaligned x
+    assert lib.dsl_linear_mxfp8(16, 6, 128, 16, 16, 64, 16, 128, None) == dsl.DSL_EINVAL  # workspace alignment
+
+
+def test_linear_workspace_holds_partials_when_split():
+    """Few output tiles split K (partials in the workspace); many do not."""
+    if not os.path.exists(dsl.LIB_PATH):
+        pytest.skip("libdsl.so not built")
+    wide = dsl.dsl_linear_workspace_bytes(6, 32768, 4096)
+    assert wide == 6 * 4096 * 2  # 2048 tiles of whole K: no partials
+    narrow = dsl.dsl_linear_workspace_bytes(6, 1024, 4096)
+    assert narrow > 6 * 4096 * 2 and (narrow - 6 * 4096 * 2) % (6 * 1024 * 4) == 0

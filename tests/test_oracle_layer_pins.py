@@ -424,3 +424,18 @@ def test_chained_layer_input_is_previous_output():
         np.testing.assert_array_equal(one["out"], res["layers"][l]["out"])
         np.testing.assert_array_equal(cl, caches[l])
         x = one["out"]
+
+
+# ---------------------------------------------------------------- the skinny head linear
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (6, 96, 384), (13, 32, 1024)])
+def test_skinny_mxfp8_linear_against_torch(M, N, K):
+    """The oracle of the draft head GEMMs is mxfp8_linear: MXq(x) . W^T in float32.  Checked
+    against a torch float64 product of the torch-side MX quantization and float8 decode above,
+    on bf16 rows off the MXFP8 grid."""
+    rng = np.random.default_rng(M * 1000 + N + K)
+    w, ws = synth.gen_mxfp8_weight(N, K, 1.5 / math.sqrt(K), rng)
+    x = synth.gen_x(synth.CONFIGS["mid"].replace(hidden=K), rng, M)
+    got = L.mxfp8_linear(__import__("oracle.formats", fromlist=["bf16_value"]).bf16_value(x), w, ws)
+    want = _f32r(_mxq(_bf16_from_bits(x)) @ _w_mx8(w, ws).T).numpy()
+    np.testing.assert_array_equal(got, want)
