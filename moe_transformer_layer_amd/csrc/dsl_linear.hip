@@ -20,7 +20,7 @@
 
 namespace dsl {
 
-constexpr int kLinWaves = 2048;  // tasks the split targets (8 waves on each of 256 compute units)
+constexpr int kLinWaves = 1024;  // split K only while the output tiles fill fewer waves (half of the 2048)
 
 // MXFP8 of each 32-block of the rows, one thread per block
 __global__ void __launch_bounds__(256) lin_mxq_kernel(const uint16_t *x, uint16_t *xq, int M, int K) {

@@ -115,7 +115,7 @@ def test_linear_workspace_holds_partials_when_split():
     """Few output tiles split K (partials in the workspace); many do not."""
     if not os.path.exists(dsl.LIB_PATH):
         pytest.skip("libdsl.so not built")
-    wide = dsl.dsl_linear_workspace_bytes(6, 32768, 4096)
-    assert wide == 6 * 4096 * 2  # 2048 tiles of whole K: no partials
+    wide = dsl.dsl_linear_workspace_bytes(6, 32320, 4096)
+    assert wide == 6 * 4096 * 2  # 2020 tiles of whole K: no partials
     narrow = dsl.dsl_linear_workspace_bytes(6, 1024, 4096)
     assert narrow > 6 * 4096 * 2 and (narrow - 6 * 4096 * 2) % (6 * 1024 * 4) == 0
