@@ -294,42 +294,55 @@ __device__ __forceinline__ uint64_t load_codes(const uint8_t *p) {
   else return ldg(p);
 }
 
-// One (row, head, split): scores q . k / sqrt(D) over up to 32 keys of the row's key set,
-// with k = v = scale * e4m3(codes) of the record; returns the partial max, the sum of
-// exponentials and (lane l: dims [V l, V l + V)) the exponential-weighted sum of values.
-// Lane j < 32 reads key j's record offset and scale; each key's offset reaches the wave
-// as a scalar (readlane), every lane loads its V dims of all 32 keys in one batch and
-// keeps them in registers for the value pass, and the 32 dot products are summed across
-// the wave by the transposing butterfly, 16 keys at a time.
-template <int V>
+// One (row, head, split): scores q . k / sqrt(D) over up to KS keys (16 or 32) of the
+// row's key set, with k = v = scale * e4m3(codes) of the record; returns the partial max,
+// the sum of exponentials and (lane l: dims [V l, V l + V)) the exponential-weighted sum
+// of values.  Lane j < KS reads key j's record offset and scale; each key's offset
+// reaches the wave as a scalar (readlane), every lane loads its V dims of all KS keys in
+// one batch and keeps them in registers for the value pass, and the dot products are
+// summed across the wave by the transposing butterfly, 16 keys at a time.  The records
+// need only the step's own records and key offsets (the caller's wait before the call);
+// q, which comes later in the stage chain, is waited for (wait_q) after the record loads
+// are issued, so they are in flight during that wait (EARLY; else the caller has waited
+// for q as well, and q is loaded with the first records: the general kernel's choice,
+// measured faster at 48 rows).
+template <int V, int KS, bool EARLY, class WaitQ>
 __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int m, int hh, int sp, int lane,
-                                          float &mx_out, float &l_out, float (&o)[V]) {
+                                          float &mx_out, float &l_out, float (&o)[V], WaitQ wait_q) {
+  static_assert(KS == 16 || KS == 32, "16 or 32 keys per split");
   const int D = p.D, H = p.H;
   const int keys = p.swa > 0 ? p.swa : p.W;
-  const int j0 = sp * kSplitKeys;
-  int64_t myoff = -1;
-  if (lane < kSplitKeys && j0 + lane < keys) myoff = ldg(p.s.keyoff + (size_t)m * keys + j0 + lane);
-  const float mysc = myoff >= 0 ? ldg(reinterpret_cast<const float *>(kv.base + myoff + D)) : 0.f;
+  const int j0 = sp * KS;
   const int nks = p.qr / p.pl.kc_qb;
   const size_t qstride = (size_t)p.M * H * D;
   const float *qp = p.s.p_q + (size_t)m * H * D + (size_t)hh * D + lane * V;
   float q[V];
-  load_sum_f32<V>(qp, qstride, nks, q);
+  int64_t myoff = -1;
+  if (lane < KS && j0 + lane < keys) myoff = ldg(p.s.keyoff + (size_t)m * keys + j0 + lane);
+  const float mysc = myoff >= 0 ? ldg(reinterpret_cast<const float *>(kv.base + myoff + D)) : 0.f;
+  if constexpr (!EARLY) {
+    wait_q();
+    load_sum_f32<V>(qp, qstride, nks, q);
+  }
   const uint32_t olo = (uint32_t)(uint64_t)myoff, ohi = (uint32_t)((uint64_t)myoff >> 32);
   // key j's record offset, as a scalar
   auto key_off = [&](int j) -> int64_t {
     return (int64_t)(((uint64_t)__builtin_amdgcn_readlane(ohi, j) << 32) | __builtin_amdgcn_readlane(olo, j));
   };
-  // every lane's V dims of the 32 keys, loaded in one batch and kept for the value pass
-  uint64_t codes[kSplitKeys];
+  // every lane's V dims of the KS keys, loaded in one batch and kept for the value pass
+  uint64_t codes[KS];
 #pragma unroll
-  for (int j = 0; j < kSplitKeys; j++) {
+  for (int j = 0; j < KS; j++) {
     const int64_t off = key_off(j);
     codes[j] = off >= 0 ? load_codes<V>(kv.base + off + lane * V) : 0ull;
   }
-  float sc[2];
+  if constexpr (EARLY) {
+    wait_q();
+    load_sum_f32<V>(qp, qstride, nks, q);
+  }
+  float sc[KS / 16];
 #pragma unroll
-  for (int hf = 0; hf < 2; hf++) {
+  for (int hf = 0; hf < KS / 16; hf++) {
     float d[16];
 #pragma unroll
     for (int j = 0; j < 16; j++) {
@@ -342,9 +355,13 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
     }
     sc[hf] = wave_transpose_sum<16>(d, lane);  // lane L: key 16 hf + (L >> 2)
   }
-  // lane j < 32: the score of key j
-  const float s0 = __shfl(sc[0], 4 * (lane & 15), kWave), s1 = __shfl(sc[1], 4 * (lane & 15), kWave);
-  const float my = myoff >= 0 ? (lane < 16 ? s0 : s1) * mysc * p.attn_scale : -INFINITY;
+  // lane j < KS: the score of key j
+  float sj = __shfl(sc[0], 4 * (lane & 15), kWave);
+  if constexpr (KS == 32) {
+    const float s1 = __shfl(sc[1], 4 * (lane & 15), kWave);
+    sj = lane < 16 ? sj : s1;
+  }
+  const float my = myoff >= 0 ? sj * mysc * p.attn_scale : -INFINITY;
   const float mx = wave_max(my);
   const float pj = my == -INFINITY ? 0.f : expf(my - mx);
   const float l = wave_sum(pj);
@@ -352,11 +369,11 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   // values: the same codes, weighted by exp(score - max) * scale (the empty asm makes
   // the compiler decode them again here instead of keeping all decoded values live)
 #pragma unroll
-  for (int j = 0; j < kSplitKeys; j++) asm volatile("" : "+v"(codes[j]));
+  for (int j = 0; j < KS; j++) asm volatile("" : "+v"(codes[j]));
 #pragma unroll
   for (int v = 0; v < V; v++) o[v] = 0.f;
 #pragma unroll
-  for (int j = 0; j < kSplitKeys; j++) {
+  for (int j = 0; j < KS; j++) {
     const float fj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), j));
     float c[V];
     decode_codes<V>(codes[j], c);
@@ -367,12 +384,29 @@ __device__ __forceinline__ void attn_item(const Params &p, const dsl_kv &kv, int
   l_out = l;
 }
 
+// The log-sum-exp combine of S split partials (max, sum, output) of one head dim d, in
+// split order: o = sum_s e_s o_s / sum_s e_s l_s with e_s = exp(max_s - max) (the same
+// operations, in the same order, as the one-wave combine of st_attention_v).
+__device__ __forceinline__ float attn_combine_dim(const float *lo_, const float *lml, int S, int D, int d) {
+  float mx = -INFINITY;
+  for (int s = 0; s < S; s++) mx = fmaxf(mx, lml[2 * s]);
+  float L = 0.f, o = 0.f;
+  for (int s = 0; s < S; s++) {
+    const float ls = lml[2 * s + 1];
+    if (!(ls > 0.f)) continue;
+    const float e = expf(lml[2 * s] - mx);
+    L += ls * e;
+    o += lo_[s * D + d] * e;
+  }
+  return L > 0.f ? o / L : o;
+}
+
 // Attention and the log-sum-exp combine in one stage: a block takes P (row, head) items
 // at a time (one if the grid has a block per item, else 8 / S), one wave per split; the
 // splits' partials meet in LDS (lds: 8 D + 16 floats), where one wave per item combines
 // them, quantizes the output to MXFP8 (a 32-block spans 32 / V lanes) and stores it.
 // Pad rows give zeros.
-template <int V>
+template <int V, bool EARLY = false>
 __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds,
                                                const unsigned *hb, int l) {
   const int S = p.S, D = p.D;
@@ -389,13 +423,18 @@ __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, c
       float mx = -INFINITY, l_ = 0.f, o[V];
 #pragma unroll
       for (int v = 0; v < V; v++) o[v] = 0.f;
-      if (p.ho) {
-        // the head's q (every wq_b task of its columns) and the step's records and key offsets
-        ho_wait(p.sync, kHoQb + hh, hb[kHoQb + hh] + (unsigned)(l + 1) * ho_per_qb(p), lane);
-        ho_wait(p.sync, kHoKv, hb[kHoKv] + (unsigned)(l + 1) * (unsigned)(2 * p.M), lane);
-      }
+      // the head's q (every wq_b task of its columns) and the step's records and key
+      // offsets; with EARLY the q wait comes once the record loads are issued
+      auto wait_q = [&] {
+        if (p.ho) ho_wait(p.sync, kHoQb + hh, hb[kHoQb + hh] + (unsigned)(l + 1) * ho_per_qb(p), lane);
+      };
+      if constexpr (!EARLY) wait_q();
+      if (p.ho) ho_wait(p.sync, kHoKv, hb[kHoKv] + (unsigned)(l + 1) * (unsigned)(2 * p.M), lane);
       // a pad row's key offsets are all -1, so its item gives zeros
-      attn_item<V>(p, kv, m, hh, sp, lane, mx, l_, o);
+      if constexpr (EARLY)
+        attn_item<V, kSplitKeys, true>(p, kv, m, hh, sp, lane, mx, l_, o, wait_q);
+      else
+        attn_item<V, kSplitKeys, false>(p, kv, m, hh, sp, lane, mx, l_, o, [] {});
 #pragma unroll
       for (int v = 0; v < V; v++) lo_[w * D + lane * V + v] = o[v];
       if (lane == 0) {
@@ -430,6 +469,57 @@ __device__ __forceinline__ void st_attention_v(const Params &p, const Ctx &cx, c
     }
     __syncthreads();
   }
+}
+
+// The narrow kernel's attention (at most 8 rows, head dim 512: the grid has a block per
+// item): a block's (row, head) item, one wave per split of KS keys (16 when the row's
+// keys fit 8 such splits, else 32), the record loads issued before the wait on q; then
+// every wave combines 64 of the head's 512 dims (one per lane) and stores them, and once
+// all eight have drained their stores, one counts the item for its head.  Each wave's
+// serial work (the item's dot products and value sums, the combine) is what sets this
+// stage's time, so the keys and the combine are spread over all eight waves.
+template <int KS>
+__device__ __forceinline__ void st_attention_narrow_ks(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds,
+                                                       const unsigned *hb, int l, int S) {
+  constexpr int V = 8, D = 512;
+  const int T = p.M * p.H;
+  const int w = cx.wave, lane = cx.lane;
+  float *lo_ = lds, *lml = lds + kWavesPerBlock * D;
+  for (int t = bid(); t < T; t += gridDim.x) {
+    const int m = t / p.H, hh = t - m * p.H;
+    if (w < S) {
+      float mx = -INFINITY, l_ = 0.f, o[V];
+#pragma unroll
+      for (int v = 0; v < V; v++) o[v] = 0.f;
+      if (p.ho) ho_wait(p.sync, kHoKv, hb[kHoKv] + (unsigned)(l + 1) * (unsigned)(2 * p.M), lane);
+      // a pad row's key offsets are all -1, so its item gives zeros
+      attn_item<V, KS, true>(p, kv, m, hh, w, lane, mx, l_, o, [&] {
+        if (p.ho) ho_wait(p.sync, kHoQb + hh, hb[kHoQb + hh] + (unsigned)(l + 1) * ho_per_qb(p), lane);
+      });
+#pragma unroll
+      for (int v = 0; v < V; v++) lo_[w * D + lane * V + v] = o[v];
+      if (lane == 0) {
+        lml[2 * w] = mx;
+        lml[2 * w + 1] = l_;
+      }
+    }
+    __syncthreads();
+    float o[1] = {attn_combine_dim(lo_, lml, S, D, 64 * w + lane)};
+    mx_quant_dequant<1>(o);
+    store_bf16<1>(p.s.ob + (size_t)m * p.H * D + (size_t)hh * D + 64 * w + lane, o);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the output is at the coherence point
+    __syncthreads();
+    if (p.ho && w == 0) ho_count(p.sync, kHoAtt + hh, lane);
+  }
+}
+
+__device__ __forceinline__ void st_attention_narrow(const Params &p, const Ctx &cx, const dsl_kv &kv, float *lds,
+                                                    const unsigned *hb, int l) {
+  const int keys = p.swa > 0 ? p.swa : p.W;
+  if (keys <= 8 * 16)
+    st_attention_narrow_ks<16>(p, cx, kv, lds, hb, l, (keys + 15) / 16);
+  else
+    st_attention_narrow_ks<32>(p, cx, kv, lds, hb, l, p.S);
 }
 
 // wo_a output: sum the split-K partials, then MXFP8
@@ -1612,7 +1702,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         pa = linear_prefetch_addr<kW8T32>(cx, w.wo_a, w.wo_a_s, nullptr, p.orr, p.H * p.D, p.pl.kc_oa);
         float *lds = reinterpret_cast<float *>(&wave_lds[0][0]);
         if constexpr (NARROW) {
-          st_attention_v<8>(p, cx, kv, lds, ho_base, l);
+          st_attention_narrow(p, cx, kv, lds, ho_base, l);
         } else {
           switch (p.D) {
             case 64: st_attention_v<1>(p, cx, kv, lds, ho_base, l); break;
