@@ -92,23 +92,93 @@ __device__ __forceinline__ v2f cvt_fp8x2_f32(uint32_t w) {
 
 // ------------------------------------------------------------------ wave reductions
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// The value of lane (this lane XOR O), O a power of two below 64: the quad steps and the
+// 8-lane step by DPP (quad_perm, and row_ror:8, which within a row of 16 is the XOR), the
+// 4-lane step by a bit-masked swizzle, the 16- and 32-lane steps by the permlane swaps.
+// None of them forms an LDS address, unlike a general shuffle.
+template <int O>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int u = __float_as_int(v);
+  if constexpr (O == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (O == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (O == 4) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x101F));  // and 0x1F, or 0, xor 4
+  } else if constexpr (O == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x128, 0xF, 0xF, false));  // row_ror 8
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    return __uint_as_float((lane_id() & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(O == 32, "lane_xor: O is a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
+  }
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// The same for a step known only after unrolling
+__device__ __forceinline__ float lane_xor_n(float v, int o) {
+  switch (o) {
+    case 1: return lane_xor<1>(v);
+    case 2: return lane_xor<2>(v);
+    case 4: return lane_xor<4>(v);
+    case 8: return lane_xor<8>(v);
+    case 16: return lane_xor<16>(v);
+    default: return lane_xor<32>(v);
+  }
+}
+// v + (the value of lane XOR O): for the 16- and 32-lane steps the permlane swap's two
+// results are that pair in every lane (addition commutes, so the sum is the same bits)
+template <int O>
+__device__ __forceinline__ float sum_xor(float v) {
+  if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return v + lane_xor<O>(v);
+  }
+}
+
+// max(v, the value of lane XOR O), the same way
+template <int O>
+__device__ __forceinline__ float max_xor(float v) {
+  if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(v, lane_xor<O>(v));
+  }
+}
+
+// Sum over the wave, the same in every lane: the XOR butterfly, 32 lanes apart first
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum_xor<32>(v);
+  v = sum_xor<16>(v);
+  v = sum_xor<8>(v);
+  v = sum_xor<4>(v);
+  v = sum_xor<2>(v);
+  return sum_xor<1>(v);
 }
 // max over aligned groups of G lanes (G a power of two <= 64)
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  if constexpr (G >= 64) v = max_xor<32>(v);
+  if constexpr (G >= 32) v = max_xor<16>(v);
+  if constexpr (G >= 16) v = max_xor<8>(v);
+  if constexpr (G >= 8) v = max_xor<4>(v);
+  if constexpr (G >= 4) v = max_xor<2>(v);
+  if constexpr (G >= 2) v = max_xor<1>(v);
   return v;
 }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // Sum over the wave of V per-lane values, transposed: returns, in lane L, the total of
 // value L >> (6 - log2 V).  Lane bit 5 is resolved by a permlane32 swap, bit 4 by a
@@ -143,11 +213,11 @@ __device__ __forceinline__ float wave_transpose_sum(float (&v)[V], int lane) {
       for (int i = 0; i < n / 2; i++) {
         const float send = hi ? c[i] : c[i + n / 2];
         const float keep = hi ? c[i + n / 2] : c[i];
-        c[i] = keep + __shfl_xor(send, 1 << bit, kWave);
+        c[i] = keep + lane_xor_n(send, 1 << bit);
       }
       n /= 2;
     } else {
-      c[0] += __shfl_xor(c[0], 1 << bit, kWave);
+      c[0] += lane_xor_n(c[0], 1 << bit);
     }
   }
   if (V == 1) {

@@ -120,18 +120,20 @@ __device__ __forceinline__ int ho_t_wb(const Params &p) { return (p.h >> 4) * (p
 __device__ __forceinline__ int ho_t_rt(const Params &p) { return p.E * (p.h / p.pl.kc_router); }
 __device__ __forceinline__ int ho_t_sh(const Params &p) { return ((2 * p.Is) >> 4) * (p.h / p.pl.kc_sh13); }
 
-// q latent: sum the split-K partials, RMSNorm, MXFP8.
-template <int E>
-__device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red) {
+// q latent: sum the split-K partials, RMSNorm, MXFP8.  wait(): the caller's wait for the
+// partials, made once the norm's weights are on their way.
+template <int E, class Wait>
+__device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w, int m, float *red, Wait wait) {
   const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.qr, k = tid() * E;
   const bool act = k < n;
   float v[E], gm[E];
+  load_f32<E>(w.q_norm + k, act, gm);
+  wait();
   if (act)
     load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + k, (size_t)p.M * N, nks, v);
   else
 #pragma unroll
     for (int e = 0; e < E; e++) v[e] = 0.f;
-  load_f32<E>(w.q_norm + k, act, gm);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; e++) ss += v[e] * v[e];
@@ -144,22 +146,24 @@ __device__ __forceinline__ void qpost_row(const Params &p, const dsl_weights &w,
 }
 
 // kv latent: RMSNorm, then the fp8 record (codes e4m3(v / s), s = amax / 448, then 12
-// zero bytes) at the row's slot.
-template <int E>
+// zero bytes) at the row's slot.  wait(): the caller's wait for the partials, made once
+// the norm's weights and the record's place (position, request, block table) are on
+// their way.
+template <int E, class Wait>
 __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w, const dsl_kv &kv, int m, float *red,
-                                           uint8_t *tmp) {
+                                           uint8_t *tmp, Wait wait) {
   const int N = p.qr + p.D, nks = p.h / p.pl.kc_qkv, n = p.D, k = tid() * E;
   const bool act = k < n;
   float v[E], gm[E];
+  load_f32<E>(w.kv_norm + k, act, gm);
+  const int pos = ldg(p.pos + m);
+  const int64_t slot = pos >= 0 ? slot_of(p, kv, ldg(kv.row_req + m), pos) : (int64_t)-1;
+  wait();
   if (act)
     load_sum_f32<E>(p.s.p_qkv + (size_t)m * N + p.qr + k, (size_t)p.M * N, nks, v);
   else
 #pragma unroll
     for (int e = 0; e < E; e++) v[e] = 0.f;
-  load_f32<E>(w.kv_norm + k, act, gm);
-  // the record's place, resolved (position, request, block table) while the row reduces
-  const int pos = ldg(p.pos + m);
-  const int64_t slot = pos >= 0 ? slot_of(p, kv, ldg(kv.row_req + m), pos) : (int64_t)-1;
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; e++) ss += v[e] * v[e];
@@ -203,34 +207,36 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
   // 2 M all of a row's work is block m's)
   if ((int)gridDim.x >= 2 * p.M) {
     const int b = bid();
-    if (p.ho >= 2 && b < 2 * p.M) {
-      // hand-off: every wqkv task of the row's part (q latent, or kv latent) has stored its partials
-      if (tid() == 0) {
-        if (b < p.M)
-          ho_wait_sum8(p.sync, kHoWq, hb_sum8(hb, kHoWq) + (unsigned)(l + 1) * (unsigned)ho_t_wq(p), 0);
-        else
-          ho_wait_sum8(p.sync, kHoWkv, hb_sum8(hb, kHoWkv) + (unsigned)(l + 1) * (unsigned)ho_t_wkv(p), 0);
+    // hand-off: every wqkv task of the row's part (q latent, or kv latent) has stored its partials
+    auto wait = [&] {
+      if (p.ho >= 2) {
+        if (tid() == 0) {
+          if (b < p.M)
+            ho_wait_sum8(p.sync, kHoWq, hb_sum8(hb, kHoWq) + (unsigned)(l + 1) * (unsigned)ho_t_wq(p), 0);
+          else
+            ho_wait_sum8(p.sync, kHoWkv, hb_sum8(hb, kHoWkv) + (unsigned)(l + 1) * (unsigned)ho_t_wkv(p), 0);
+        }
+        __syncthreads();
       }
-      __syncthreads();
-    }
+    };
     if (b >= 2 * p.M && b < 3 * p.M) key_offsets_row(p, kv, b - 2 * p.M);
     if (b < p.M) {
       switch (eq) {
-        case 2: qpost_row<2>(p, w, b, red); break;
+        case 2: qpost_row<2>(p, w, b, red, wait); break;
         default:
           if constexpr (!NARROW) {
-            if (eq == 1) qpost_row<1>(p, w, b, red);
-            else if (eq == 4) qpost_row<4>(p, w, b, red);
-            else if (eq == 8) qpost_row<8>(p, w, b, red);
-            else qpost_row<16>(p, w, b, red);
+            if (eq == 1) qpost_row<1>(p, w, b, red, wait);
+            else if (eq == 4) qpost_row<4>(p, w, b, red, wait);
+            else if (eq == 8) qpost_row<8>(p, w, b, red, wait);
+            else qpost_row<16>(p, w, b, red, wait);
           }
           break;
       }
     } else if (b < 2 * p.M) {
       switch (ekv) {
-        case 1: kvpost_row<1>(p, w, kv, b - p.M, red, tmp); break;
+        case 1: kvpost_row<1>(p, w, kv, b - p.M, red, tmp, wait); break;
         default:
-          if constexpr (!NARROW) kvpost_row<2>(p, w, kv, b - p.M, red, tmp);
+          if constexpr (!NARROW) kvpost_row<2>(p, w, kv, b - p.M, red, tmp, wait);
           break;
       }
     }
@@ -247,20 +253,20 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
   }
   for (int m = bid(); m < p.M; m += gridDim.x) {
     switch (eq) {
-      case 2: qpost_row<2>(p, w, m, red); break;
+      case 2: qpost_row<2>(p, w, m, red, [] {}); break;
       default:
         if constexpr (!NARROW) {
-          if (eq == 1) qpost_row<1>(p, w, m, red);
-          else if (eq == 4) qpost_row<4>(p, w, m, red);
-          else if (eq == 8) qpost_row<8>(p, w, m, red);
-          else qpost_row<16>(p, w, m, red);
+          if (eq == 1) qpost_row<1>(p, w, m, red, [] {});
+          else if (eq == 4) qpost_row<4>(p, w, m, red, [] {});
+          else if (eq == 8) qpost_row<8>(p, w, m, red, [] {});
+          else qpost_row<16>(p, w, m, red, [] {});
         }
         break;
     }
     switch (ekv) {
-      case 1: kvpost_row<1>(p, w, kv, m, red, tmp); break;
+      case 1: kvpost_row<1>(p, w, kv, m, red, tmp, [] {}); break;
       default:
-        if constexpr (!NARROW) kvpost_row<2>(p, w, kv, m, red, tmp);
+        if constexpr (!NARROW) kvpost_row<2>(p, w, kv, m, red, tmp, [] {});
         break;
     }
   }
@@ -569,7 +575,7 @@ __device__ __forceinline__ void tq_group_quant(const Params &p, int j, int lane)
     const int m = m0 + (lane >> 3);
     float v[4];
     if (m < p.M)
-      load_sum_f32<4>(p.s.p_t + (size_t)m * N + k, (size_t)p.M * N, nks, v);
+      load_sum_f32<4, 16>(p.s.p_t + (size_t)m * N + k, (size_t)p.M * N, nks, v);  // one batch for 16 heads
     else
 #pragma unroll
       for (int e = 0; e < 4; e++) v[e] = 0.f;
@@ -680,21 +686,26 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
   const int h = p.h, nks = p.orr / p.pl.kc_ob, k = tid() * E;
   const bool act = k < h;
   for (int m = bid(); m < p.M; m += gridDim.x) {
+    // what does not depend on wo_b first (the row's position, its residual input, the
+    // norm's weights), so that those loads are in flight during the wait
+    const bool live = ldg(p.pos + m) >= 0;
+    float a[E], hr[E], gm[E];
+    if (act)
+      load_bf16<E>(xin + (size_t)m * h + k, hr);
+    else
+#pragma unroll
+      for (int e = 0; e < E; e++) hr[e] = 0.f;
+    load_f32<E>(w.ffn_norm + k, act && p.mode != kModeAttn, gm);
     if (p.ho >= 2) {
       // hand-off: every wo_b task of the layer has stored its partials
       if (tid() == 0) ho_wait_sum8(p.sync, kHoWb, hb_sum8(hb, kHoWb) + (unsigned)(l + 1) * (unsigned)ho_t_wb(p), 0);
       __syncthreads();
     }
-    const bool live = ldg(p.pos + m) >= 0;
-    float a[E], hr[E], gm[E];
-    if (act) {
+    if (act)
       load_sum_f32<E>(p.s.p_a + (size_t)m * h + k, (size_t)p.M * h, nks, a);
-      load_bf16<E>(xin + (size_t)m * h + k, hr);
-    } else {
+    else
 #pragma unroll
-      for (int e = 0; e < E; e++) a[e] = hr[e] = 0.f;
-    }
-    load_f32<E>(w.ffn_norm + k, act && p.mode != kModeAttn, gm);
+      for (int e = 0; e < E; e++) a[e] = 0.f;
 #pragma unroll
     for (int e = 0; e < E; e++) {
       a[e] = live ? a[e] : 0.f;

@@ -512,11 +512,11 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 }
 
 // v[e] = sum over ks < nks (in ks order) of p[ks * stride + e]: the loads of up to B
-// partials are issued together, then added in order, so a stage does not wait a
-// round trip per partial.
-template <int E>
+// partials (BMAX, else 32 registers' worth) are issued together, then added in order, so a
+// stage does not wait a round trip per partial.
+template <int E, int BMAX = 0>
 __device__ __forceinline__ void load_sum_f32(const float *p, size_t stride, int nks, float v[E]) {
-  constexpr int B = E >= 32 ? 1 : (E >= 4 ? 32 / E : 8);
+  constexpr int B = BMAX > 0 ? BMAX : (E >= 32 ? 1 : (E >= 4 ? 32 / E : 8));
 #pragma unroll
   for (int e = 0; e < E; e++) v[e] = 0.f;
   for (int k0 = 0; k0 < nks; k0 += B) {
