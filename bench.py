@@ -332,6 +332,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--only-m48", action="store_true", help="only the M=48 layer (for counter passes)")
     ap.add_argument("--only-draft", action="store_true", help="only the three chained draft layers at M=6")
+    ap.add_argument("--only-a8-m48", action="store_true", help="only the M=48 layer with A8W4 experts")
+    ap.add_argument("--a8-mx", action="store_true",
+                    help="with --only-a8-m48: the matrix-core experts on the scaled MX instruction")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
@@ -354,6 +357,12 @@ def main():
                           graph_replay=not args.no_graph)
         print(f"[bench] draft M=6: {draft['us_per_layer_kernel']:.1f} us/layer, {draft['gbs']:.0f} GB/s", flush=True)
         print(json.dumps({"draft_m6": draft}), flush=True)
+        return
+    if args.only_a8_m48:
+        m48_a8 = run_point(dsl, torch, "layer48_a8mx" if args.a8_mx else "layer48_a8", 48, max(2, args.copies // 2),
+                           args.steps, args.warmup, weights, graph_replay=not args.no_graph)
+        print(f"[bench] A8W4 M=48: {m48_a8['us_kernel_mean']:.1f} us/launch, {m48_a8['gbs']:.0f} GB/s", flush=True)
+        print(json.dumps({"a8w4_m48": m48_a8}), flush=True)
         return
     if args.only_m48:
         m48 = run_point(dsl, torch, "layer48", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
@@ -379,7 +388,7 @@ def main():
         draft = run_point(dsl, torch, "draft", 6, 2, args.steps, args.warmup, weights * 3,
                           graph_replay=not args.no_graph)
         print(f"[bench] draft M=6: {draft['us_per_layer_kernel']:.1f} us/layer, {draft['gbs']:.0f} GB/s", flush=True)
-    m6_a8 = m48_a8 = None
+    m6_a8 = m48_a8 = m48_a8mx = None
     if not args.only_m6:
         # the A8W4 variant: MXFP8 activations into the same MXFP4 experts (same weights)
         print("[bench] A8W4 experts: M=6 and M=48 full layer", flush=True)
@@ -387,8 +396,11 @@ def main():
                           graph_replay=False)
         m48_a8 = run_point(dsl, torch, "layer48_a8", 48, max(2, args.copies // 2), args.steps, args.warmup, weights,
                            graph_replay=False)
+        # the same A8W4 layer with the matrix-core experts on the scaled MX instruction
+        m48_a8mx = run_point(dsl, torch, "layer48_a8mx", 48, max(2, args.copies // 2), args.steps, args.warmup,
+                             weights, graph_replay=False)
         print(f"[bench] A8W4 M=6: {m6_a8['us_kernel_mean']:.1f} us/launch; M=48: {m48_a8['us_kernel_mean']:.1f} "
-              f"us/launch", flush=True)
+              f"us/launch; M=48 on the scaled MX instruction: {m48_a8mx['us_kernel_mean']:.1f} us/launch", flush=True)
     head = None
     if not args.only_m6:
         print("[bench] draft head GEMM (skinny MXFP8 linear, 6 x 4096 -> 32320)", flush=True)
@@ -433,6 +445,7 @@ def main():
         "draft_m6": draft,
         "a8w4_m6": m6_a8,
         "a8w4_m48": m48_a8,
+        "a8w4mx_m48": m48_a8mx,
         "head_gemm_m6": head,
         "warm_m6": warm,
         "cpu_baseline": cpu,

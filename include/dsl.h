@@ -67,7 +67,7 @@ extern "C" {
  * 128; the shared expert has 128x128 scale blocks); head_dim in {64, 128, 256,
  * 512}; 1 <= n_experts <= 128; 1 <= top_k <= min(8, n_experts);
  * 1 <= max_rows <= 48; 1 <= n_layers <= DSL_MAX_LAYERS; 1 <= window <= 256;
- * expert_a8 in {0, 1};
+ * expert_a8 in {0, 1, 2};
  * 0 <= swa_width <= 256 (a row's keys are split over at most 8 waves of 32 keys);
  * kv_block >= 1.  Other values: DSL_EUNSUPPORTED or DSL_EINVAL. */
 typedef struct {
@@ -87,7 +87,13 @@ typedef struct {
                           1: they take MXFP8 activations (A8W4, the pages' "a8w4
                           MoE": PR 60397, Test Plan): gate/up reads MXq(u) and down
                           reads MXq(z), each per 1x32 block of the bf16 value.  The
-                          router and the shared expert keep the bf16 u.           */
+                          router and the shared expert keep the bf16 u.
+                          2: the same A8W4 layer, with the experts on the matrix
+                          cores taking the raw e2m1 and e4m3 codes and their E8M0
+                          block exponents on the gfx950 scaled MX instruction
+                          (v_mfma_scale_f32_16x16x128_f8f6f4) instead of their
+                          exact bf16 values; same products, f32 sums in another
+                          order.                                                    */
   float norm_eps;      /* RMSNorm epsilon (1e-6)                                */
   float swiglu_limit;  /* SwiGLU clamp (7.0)                                    */
 } dsl_dims;

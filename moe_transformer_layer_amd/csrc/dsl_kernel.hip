@@ -743,30 +743,50 @@ __device__ __forceinline__ void st_ffn_norm_e(const Params &p, const dsl_weights
 
 // ============================================================== MoE
 
-// MXFP8 of 32-element blocks of bf16 rows, kept as exact bf16 values: block b of n
-// blocks (row b / per, 32 columns from 32 (b % per)) from src to dst, one thread per block.
+// MXFP8 of 32-element blocks of bf16 rows: block b of n blocks (row b / per, 32 columns from
+// 32 (b % per)) from src, one thread per block, as exact bf16 values into dst (the VALU
+// experts' operand, and the matrix-core experts' with expert_a8 = 1) and, with code set
+// (expert_a8 = 2), also as e4m3 codes and the block's E8M0 exponent into code / ex (the
+// scaled matrix instruction's operand; the same quantization, so the two agree exactly).
 // The A8W4 variant's expert inputs: "Mono decode layer for DeepSeek-V4.1-Flash on MI355X"
 // (vLLM PR 60397), Test Plan (the a8w4 MoE), with the OCP MX block rule of the layer's other
 // MXFP8 activations.
-__device__ __forceinline__ void mx_block_bf16(const uint16_t *src, uint16_t *dst, int b, int per, int ld) {
+__device__ __forceinline__ void mx_block_a8(const uint16_t *src, uint16_t *dst, uint8_t *code, uint8_t *ex, int b,
+                                            int per, int ld) {
   const size_t off = (size_t)(b / per) * ld + 32 * (b % per);
   float v[32];
   load_bf16<32>(src + off, v);
-  mx_quant_dequant<32>(v);
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; e++) am = fmaxf(am, fabsf(v[e]));
+  const uint32_t X = mx_e4m3_exponent(am);
+  const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
+  v4u cw[2] = {v4u{0, 0, 0, 0}, v4u{0, 0, 0, 0}};
+#pragma unroll
+  for (int e = 0; e < 32; e++) {
+    const uint32_t c = f32_to_e4m3(v[e] * inv);
+    v[e] = e4m3_to_f32(c) * sc;
+    cw[e >> 4][(e >> 2) & 3] |= c << (8 * (e & 3));
+  }
   store_bf16<32>(dst + off, v);
+  if (code) {
+    st16(code + off, cw[0]);
+    st16(code + off + 16, cw[1]);
+    stg(ex + off / 32, (uint8_t)X);
+  }
 }
 
 // A8W4: MXFP8 of the MoE input u [M][h] into uq, by the grid's threads in reverse order (the
 // last waves, which have no router or shared gate/up task, take the blocks first).
 __device__ __forceinline__ void st_u_quant(const Params &p, const Ctx &cx, const uint16_t *u) {
   const int per = p.h >> 5, n = p.M * per, nt = cx.nw * kWave;
-  for (int b = nt - 1 - (cx.gw * kWave + cx.lane); b < n; b += nt) mx_block_bf16(u, p.s.uq, b, per, p.h);
+  for (int b = nt - 1 - (cx.gw * kWave + cx.lane); b < n; b += nt) mx_block_a8(u, p.s.uq, p.a8 == 2 ? p.s.uq8 : nullptr, p.s.uqe, b, per, p.h);
 }
 
 // A8W4: MXFP8 of the routed SwiGLU outputs z [pairs][I] into zq (one thread per block).
 __device__ __forceinline__ void st_z_quant(const Params &p, const Routing &R) {
   const int per = p.I >> 5, n = R.np * per;
-  for (int b = bid() * kThreads + tid(); b < n; b += gridDim.x * kThreads) mx_block_bf16(p.s.zr, p.s.zq, b, per, p.I);
+  for (int b = bid() * kThreads + tid(); b < n; b += gridDim.x * kThreads) mx_block_a8(p.s.zr, p.s.zq, p.a8 == 2 ? p.s.zq8 : nullptr, p.s.zqe, b, per, p.I);
 }
 
 // Router partial logits of one (expert e, K chunk c) task for all rows: lane l takes
@@ -1050,7 +1070,19 @@ __device__ __forceinline__ void routed_gate_up_task(const Params &p, const dsl_w
   }
   const WStream ws[2] = {wstream<kW4>(W, S8, nullptr, h, tile * 16 + i, 0, g),
                          wstream<kW4>(W, S8, nullptr, h, I + tile * 16 + i, 0, g)};
-  tiles<kW4, 2, NCG>(ws, h >> 7, xrow, xok, 32 * g, g, acc);
+  if (p.a8 == 2) {
+    // A8W4 on the scaled matrix instruction: the same rows' MXFP8 codes and exponents
+    const uint8_t *xr8[NCG], *xe[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; c++) {
+      const size_t r = xok[c] ? (size_t)R.pair_row[p0 + 16 * c + i] : 0;
+      xr8[c] = p.s.uq8 + r * h;
+      xe[c] = p.s.uqe + r * (h >> 5);
+    }
+    tiles_a8<2, NCG>(ws, h >> 7, xr8, xe, xok, g, acc);
+  } else {
+    tiles<kW4, 2, NCG>(ws, h >> 7, xrow, xok, 32 * g, g, acc);
+  }
 #pragma unroll
   for (int c = 0; c < NCG; c++) {
     const int j = 16 * c + i;
@@ -1087,7 +1119,19 @@ __device__ __forceinline__ void routed_down_task(const Params &p, const dsl_weig
   WStream ws[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; tt++) ws[tt] = wstream<kW4>(W, S8, nullptr, I, (tile * NT + tt) * 16 + i, 0, g);
-  tiles<kW4, NT, NCG>(ws, I >> 7, xrow, xok, 32 * g, g, acc);
+  if (p.a8 == 2) {
+    // A8W4 on the scaled matrix instruction: the pairs' MXFP8 codes and exponents
+    const uint8_t *xr8[NCG], *xe[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; c++) {
+      const size_t r = (size_t)(p0 + (xok[c] ? 16 * c + i : 0));
+      xr8[c] = p.s.zq8 + r * I;
+      xe[c] = p.s.zqe + r * (I >> 5);
+    }
+    tiles_a8<NT, NCG>(ws, I >> 7, xr8, xe, xok, g, acc);
+  } else {
+    tiles<kW4, NT, NCG>(ws, I >> 7, xrow, xok, 32 * g, g, acc);
+  }
 #pragma unroll
   for (int tt = 0; tt < NT; tt++)
 #pragma unroll
@@ -1993,7 +2037,7 @@ static int validate_dims(const dsl_dims *d) {
     return fail(DSL_EUNSUPPORTED, "window %d / swa_width %d: at most %d keys per row (8 splits of %d)", d->window,
                 d->swa_width, 8 * kSplitKeys, kSplitKeys);
   if (d->kv_block < 1) return fail(DSL_EINVAL, "kv_block %d < 1", d->kv_block);
-  if (d->expert_a8 != 0 && d->expert_a8 != 1) return fail(DSL_EINVAL, "expert_a8 %d is neither 0 nor 1", d->expert_a8);
+  if (d->expert_a8 < 0 || d->expert_a8 > 2) return fail(DSL_EINVAL, "expert_a8 %d is not 0, 1 or 2", d->expert_a8);
   if (!(d->norm_eps >= 0.f) || !(d->swiglu_limit > 0.f))
     return fail(DSL_EINVAL, "norm_eps must be >= 0 and swiglu_limit > 0");
   return 0;
@@ -2041,6 +2085,10 @@ static size_t layout(const dsl_layer *L, int M, Scratch *s, char *base) {
   s->p_shd = (float *)take((Is / pl.kc_shd) * m * h * 4);
   s->uq = d.expert_a8 ? (uint16_t *)take(m * h * 2) : nullptr;
   s->zq = d.expert_a8 ? (uint16_t *)take(m * k * I * 2) : nullptr;
+  s->uq8 = d.expert_a8 == 2 ? (uint8_t *)take(m * h) : nullptr;
+  s->uqe = d.expert_a8 == 2 ? (uint8_t *)take(m * h / 32) : nullptr;
+  s->zq8 = d.expert_a8 == 2 ? (uint8_t *)take(m * k * I) : nullptr;
+  s->zqe = d.expert_a8 == 2 ? (uint8_t *)take(m * k * I / 32) : nullptr;
   return (off + 255) & ~(size_t)255;
 }
 

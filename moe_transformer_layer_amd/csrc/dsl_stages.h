@@ -63,11 +63,16 @@ struct Scratch {
   float *p_shd;            // [nks][M][h]
   uint16_t *uq;            // A8W4: MXFP8(u) as exact bf16 values [M][h], the routed gate/up input
   uint16_t *zq;            // A8W4: MXFP8(z) as exact bf16 values [M*k][I], the routed down input
+  uint8_t *uq8;            // A8W4: the same MXFP8(u) as e4m3 codes [M][h] ...
+  uint8_t *uqe;            // ... and E8M0 block exponents [M][h / 32] (the matrix-core experts' operand)
+  uint8_t *zq8;            // A8W4: MXFP8(z) as e4m3 codes [M*k][I] ...
+  uint8_t *zqe;            // ... and E8M0 block exponents [M*k][I / 32]
 };
 
 struct Params {
   int h, H, D, qr, orr, W, swa, E, k, I, Is, B, n_layers;
-  int a8;  // the routed experts take MXFP8 activations (A8W4)
+  int a8;  // the routed experts take MXFP8 activations (A8W4): 1 as exact bf16 values, 2 as
+           // codes on the scaled matrix instruction
   float eps, lim, attn_scale;
   int M, mode, S;
   int ho;  // the attention's producers hand off through counters instead of grid barriers
@@ -365,6 +370,134 @@ __device__ __forceinline__ void tiles_pipe1(const WStream ws[NT], int nsteps, co
 template <int FMT>
 __device__ __forceinline__ bool scales_aligned(const WStream &ws) {
   return FMT == kW8B128 ? ((uintptr_t)ws.s32 & 15) == 0 : ((uintptr_t)ws.s8 & 15) == 0;
+}
+
+// ------------------------------------------------------------ A8W4 on the scaled matrix instruction
+//
+// With MXFP8 activations the routed experts' matrix-core tiles multiply raw codes:
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes the MXFP4 weights (A, e2m1) and the MXFP8
+// activations (B, e4m3) as they are stored, with one E8M0 exponent per 32-element block of
+// each, and sums the 128 exactly scaled products of a K step in f32.  No decode, and one
+// instruction per step and tile pair instead of four, so the same registers hold a ring
+// twice as deep as the bf16 tiles' (8 steps of weights).
+// Operand layouts (read off the instruction on gfx950): A lane (i, g) holds weight row i,
+// K [32 g, 32 g + 32) of the step, 16 bytes in K order; B lane (j, g) holds activation row
+// j, K [16 g, 16 g + 16) in its first 16 bytes and K [64 + 16 g, 64 + 16 g + 16) in the
+// next 16; each lane gives the exponent of block g (K [32 g, 32 g + 32)) of its row; the
+// result is laid out as the bf16 instruction's (lane l: weight rows 4 (l / 16) + r,
+// activation row l % 16).
+
+// One step's B fragment of one group of 16 activation rows (codes), zero past the group's
+// end: the register pair is cleared, then only the group's lanes load into it (no select
+// after the loads, which would wait for them)
+union B8 {
+  v8i v;
+  v4u h[2];
+};
+__device__ __forceinline__ void load_b8(B8 &b, const uint8_t *row, bool ok, int k) {
+  b.v = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  if (ok) {
+    b.h[0] = ld16(row + k);
+    b.h[1] = ld16(row + k + 64);
+  }
+}
+
+__device__ __forceinline__ v4f mfma_a8w4(const v4u &a, const B8 &bb, v4f c, uint32_t sa, uint32_t sb) {
+  const v8i b = bb.v;
+  const v4i a4 = __builtin_bit_cast(v4i, a);
+  const v8i av = __builtin_shufflevector(a4, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// NT MXFP4 weight tiles times NCG groups of 16 MXFP8 activation rows (codes xrow, block
+// exponents xex; xok: the lane's row exists) over nsteps 128-wide K steps, nsteps % P == 0:
+// the weights (and each lane's exponent byte of them) P steps ahead and the activations
+// (and theirs) PB steps ahead in register rings, each step's weight loads issued before its
+// activation loads (loads complete in issue order, so a wait for an activation then
+// waits for no weight issued after it).  The result as tiles_pipe4's.
+template <int NT, int NCG, int P>
+__device__ __forceinline__ void tiles_a8w4(const WStream ws[NT], int nsteps, const uint8_t *const xrow[NCG],
+                                           const uint8_t *const xex[NCG], const bool xok[NCG], int g, v4f acc[NT][NCG]) {
+  constexpr int PB = NCG == 1 ? P : (NCG == 2 ? P / 2 : (P >= 4 ? P / 4 : 1));
+  v4u ra[P][NT];
+  uint32_t sa[P][NT];  // the step's four exponent bytes of the lane's weight row; byte g is the lane's
+  B8 rb[PB][NCG];
+  uint32_t sb[PB][NCG];  // likewise for the lane's activation row
+#pragma unroll
+  for (int j = 0; j < P; j++)
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+      ra[j][tt] = ld16(ws[tt].w + 64 * j);
+      sa[j][tt] = ldg(reinterpret_cast<const uint32_t *>(ws[tt].s8 + 4 * j));
+    }
+#pragma unroll
+  for (int j = 0; j < PB; j++)
+#pragma unroll
+    for (int c = 0; c < NCG; c++) {
+      load_b8(rb[j][c], xrow[c], xok[c], 128 * j + 16 * g);
+      sb[j][c] = ldg(reinterpret_cast<const uint32_t *>(xex[c] + 4 * j));
+    }
+  for (int s = 0; s < nsteps; s += P) {
+    const bool more = s + P < nsteps;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+      const int st = s + j;
+#pragma unroll
+      for (int c = 0; c < NCG; c++)
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++)
+          acc[tt][c] = mfma_a8w4(ra[j][tt], rb[j % PB][c], acc[tt][c], (sa[j][tt] >> (8 * g)) & 0xFFu,
+                                 (sb[j % PB][c] >> (8 * g)) & 0xFFu);
+      if (more) {
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+          ra[j][tt] = ld16(ws[tt].w + 64 * (st + P));
+          sa[j][tt] = ldg(reinterpret_cast<const uint32_t *>(ws[tt].s8 + 4 * (st + P)));
+        }
+      }
+      if (st + PB < nsteps) {
+#pragma unroll
+        for (int c = 0; c < NCG; c++) {
+          load_b8(rb[j % PB][c], xrow[c], xok[c], 128 * (st + PB) + 16 * g);
+          sb[j % PB][c] = ldg(reinterpret_cast<const uint32_t *>(xex[c] + 4 * (st + PB)));
+        }
+      }
+    }
+  }
+}
+
+// Any step count: one step at a time (the small shapes)
+template <int NT, int NCG>
+__device__ __forceinline__ void tiles_a8w4_1(const WStream ws[NT], int nsteps, const uint8_t *const xrow[NCG],
+                                             const uint8_t *const xex[NCG], const bool xok[NCG], int g, v4f acc[NT][NCG]) {
+  for (int st = 0; st < nsteps; st++) {
+    v4u ra[NT];
+    B8 rb[NCG];
+    uint32_t sa[NT], sb[NCG];
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+      ra[tt] = ld16(ws[tt].w + 64 * st);
+      sa[tt] = ldg(ws[tt].s8 + 4 * st + g);
+    }
+#pragma unroll
+    for (int c = 0; c < NCG; c++) {
+      load_b8(rb[c], xrow[c], xok[c], 128 * st + 16 * g);
+      sb[c] = ldg(xex[c] + 4 * st + g);
+    }
+#pragma unroll
+    for (int c = 0; c < NCG; c++)
+#pragma unroll
+      for (int tt = 0; tt < NT; tt++) acc[tt][c] = mfma_a8w4(ra[tt], rb[c], acc[tt][c], sa[tt], sb[c]);
+  }
+}
+
+template <int NT, int NCG>
+__device__ __forceinline__ void tiles_a8(const WStream ws[NT], int nsteps, const uint8_t *const xrow[NCG],
+                                         const uint8_t *const xex[NCG], const bool xok[NCG], int g, v4f acc[NT][NCG]) {
+  if (nsteps % 8 == 0)
+    tiles_a8w4<NT, NCG, 4>(ws, nsteps, xrow, xex, xok, g, acc);
+  else
+    tiles_a8w4_1<NT, NCG>(ws, nsteps, xrow, xex, xok, g, acc);
 }
 
 // Pipelined path when the step count and scale alignment allow it (always so when the

@@ -41,7 +41,7 @@ class Dims:
     kv_block: int
     max_rows: int
     n_layers: int = 1
-    expert_a8: int = 0  # 1: the routed experts take MXFP8 activations (A8W4)
+    expert_a8: int = 0  # 1: the routed experts take MXFP8 activations (A8W4); 2: the same on the scaled MX instruction
     norm_eps: float = 1e-6
     swiglu_limit: float = 7.0
 
@@ -81,13 +81,18 @@ CONFIGS = {
 }
 # The same workloads with MXFP8 activations into the MXFP4 experts (A8W4); each draws
 # the same weights and inputs as the workload it is named after.
+# (_a8mx: the same A8W4 layer on the scaled MX matrix instruction; the same draws.)
 for _n in ("moe6", "layer48", "mid"):
     CONFIGS[_n + "_a8"] = CONFIGS[_n].replace(expert_a8=1)
+    CONFIGS[_n + "_a8mx"] = CONFIGS[_n].replace(expert_a8=2)
 
 
 def base_name(name: str) -> str:
-    """The workload whose draws a configuration shares (an _a8 variant's base)."""
-    return name[:-3] if name.endswith("_a8") else name
+    """The workload whose draws a configuration shares (an A8W4 variant's base)."""
+    for suffix in ("_a8mx", "_a8"):
+        if name.endswith(suffix):
+            return name[: -len(suffix)]
+    return name
 
 
 def _bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -4,7 +4,8 @@ same seeded inputs.  Seeds come from tests/golden/seeds.json (written by
 make_seeds.py with the oracle alone); each test re-checks the top-k gap rule.
 
   MoE stage alone, M = 6, top-3, W4A16 and A8W4 (moe6, moe6_a8)
-  full layer with A8W4 experts, M = 48 and M = 6 (layer48_a8)
+  full layer with A8W4 experts, M = 48 and M = 6 (layer48_a8, and layer48_a8mx on the
+  scaled MX matrix instruction)
   attention half alone, M = 48 (8 x 6 rows)     (attn48)
   full layer, top-6, M = 48 and M = 6           (layer48)
   full layer at the narrow kernel's widths: 2, 8, 5 + a pad row, 7 + a pad row
@@ -208,9 +209,9 @@ def _run_chain(dsl, name, key):
     er.raise_any(key, _say)
 
 
-@pytest.mark.parametrize("name", ["moe6", "moe6_a8"])
+@pytest.mark.parametrize("name", ["moe6", "moe6_a8", "moe6_a8mx"])
 def test_moe_stage_m6_top3(dsl, name):
-    sd = _seeded(name)
+    sd = _seeded(synth.base_name(name) + ("_a8" if name != synth.base_name(name) else ""))
     layers, dw = _device_weights(dsl, name, sd["weights_seed"])
     case = synth.make_case(name, sd["seed"], layers=layers)
     d = case.dims
@@ -287,11 +288,13 @@ def test_draft_three_layers(dsl, M):
     _run_chain(dsl, "draft", f"draft_m{M}")
 
 
-# A8W4: MXFP8 activations into the routed experts, the full layer at 48 and at 6 rows
+# A8W4: MXFP8 activations into the routed experts, the full layer at 48 and at 6 rows, with
+# the matrix-core experts on exact bf16 values (layer48_a8) and on the scaled MX
+# instruction (layer48_a8mx: the same draws and the same oracle)
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("M", [48, 6])
-def test_full_layer_a8(dsl, M):
-    _run_decode(dsl, "layer48_a8", f"layer48_a8_m{M}", narrow=M <= 8)
+@pytest.mark.parametrize("name,M", [("layer48_a8", 48), ("layer48_a8", 6), ("layer48_a8mx", 48), ("layer48_a8mx", 6)])
+def test_full_layer_a8(dsl, name, M):
+    _run_decode(dsl, name, f"layer48_a8_m{M}", narrow=M <= 8)
 
 
 def test_draft_three_layers_m6_pad(dsl):

@@ -86,11 +86,13 @@ def test_mid_draft_two_layers(dsl):
 
 
 # A8W4 (MXFP8 activations into the routed experts) either side of 8 rows, with a pad row
+# (mid_a8mx: the matrix-core experts on the scaled MX instruction, K steps one at a time)
+@pytest.mark.parametrize("name", ["mid_a8", "mid_a8mx"])
 @pytest.mark.parametrize("n_req,rows,n_pad", [(1, 6, 1), (2, 6, 0)])
-def test_mid_layer_a8(dsl, n_req, rows, n_pad):
-    case, (res, caches) = _decode_case("mid_a8", f"mid_a8_{n_req}x{rows}+{n_pad}", first=800,
+def test_mid_layer_a8(dsl, name, n_req, rows, n_pad):
+    case, (res, caches) = _decode_case(name, f"mid_a8_{n_req}x{rows}+{n_pad}", first=800,
                                        n_req=n_req, rows_per_req=rows, n_pad=n_pad)
-    assert case.dims.expert_a8 == 1
+    assert case.dims.expert_a8 == (2 if name.endswith("mx") else 1)
     run_decode(dsl, case, res, caches, W_TOL_LAYER)
 
 
@@ -109,7 +111,7 @@ def test_mid_attention_only(dsl):
     check_records(case.dims, gc[0], caches[0], case.kv.cache[0])
 
 
-@pytest.mark.parametrize("name", ["mid", "mid_a8"])
+@pytest.mark.parametrize("name", ["mid", "mid_a8", "mid_a8mx"])
 def test_mid_moe_only(dsl, name):
     d = synth.CONFIGS[name]
 
