@@ -1656,6 +1656,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   __shared__ unsigned cb_base[kWavesPerBlock];  // each wave's combine group counter before this layer
   const unsigned nb = gridDim.x;
   __shared__ unsigned ho_base[kHoSlots];         // hand-off counters before this launch
+  __shared__ unsigned rt_flag;                   // layer + 1 once this block has seen every router task
   int mode, n_layers, a8, ho, Mrows;
   SyncWords *sw;
   Tracer tr;
@@ -1676,6 +1677,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   // no producer of the launch counts before every block has arrived at the first barrier
   if (ho && tid() < kHoSlots)
     ho_base[tid()] = __hip_atomic_load(gptr(&sw->ho[tid()][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0) rt_flag = 0u;
   const bool moe_mode = mode == kModeMoe;
   // full hand-offs (ho >= 2) also replace the barriers after wqkv, wo_b, the FFN norm and
   // (steps whose top-k runs in every block, bf16 expert inputs) the router
@@ -1859,8 +1861,21 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         // no grid barrier between the router and the experts: every block selects the
         // experts of every row itself (with hand-offs, once every router task has stored
         // its partial logits)
-        if (ho_router && cx.wave < p.M)
-          ho_wait_sum8(p.sync, kHoRt, hb_sum8(ho_base, kHoRt) + (unsigned)(l + 1) * (unsigned)ho_t_rt(p), cx.lane);
+        // The router counters are polled by one wave per block, which then raises the
+        // block's flag in LDS for its row waves: with every row wave of every block polling
+        // them (M x 256 pollers), the polls delayed the counters' own increments by several
+        // microseconds.
+        if (ho_router && cx.wave < p.M) {
+          if (cx.wave == 0) {
+            ho_wait_sum8(p.sync, kHoRt, hb_sum8(ho_base, kHoRt) + (unsigned)(l + 1) * (unsigned)ho_t_rt(p), cx.lane);
+            if (cx.lane == 0) __hip_atomic_store(&rt_flag, (unsigned)(l + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else if (cx.lane == 0) {
+            // wave 0 of the block always gets here (every step has a row 0), so this ends
+            while (__hip_atomic_load(&rt_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != (unsigned)(l + 1))
+              __builtin_amdgcn_s_sleep(1);
+          }
+          asm volatile("" ::: "memory");  // the logit loads stay after the wait
+        }
         topk_in_block(p, cx, R, moe_mode, last && bid() == 0 ? p.taps.logits : nullptr);
         tr.mark();
         tr.mark();
