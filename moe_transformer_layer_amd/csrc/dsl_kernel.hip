@@ -794,9 +794,9 @@ __device__ __forceinline__ void st_z_quant(const Params &p, const Routing &R) {
 // lane partials of 8 rows at a time are summed across the wave by the transposing
 // butterfly (lane L then holds row L >> 3), written to logits[c][m][e].  Each batch of
 // loads is issued before any arithmetic uses it.
-template <int J>
+template <int J, class Wait>
 __device__ __forceinline__ void router_task_j(const Params &p, const float *__restrict__ Wr, const uint16_t *u, int e,
-                                              int c, int lane) {
+                                              int c, int lane, Wait wait) {
   const int h = p.h, kc = p.pl.kc_router;
   float4 wv[J][2];
   bool on[J];
@@ -809,6 +809,8 @@ __device__ __forceinline__ void router_task_j(const Params &p, const float *__re
     wv[j][0] = make_float4(__uint_as_float(w0[0]), __uint_as_float(w0[1]), __uint_as_float(w0[2]), __uint_as_float(w0[3]));
     wv[j][1] = make_float4(__uint_as_float(w1[0]), __uint_as_float(w1[1]), __uint_as_float(w1[2]), __uint_as_float(w1[3]));
   }
+  // the weights do not depend on the step: they are on their way before the wait for u
+  wait();
   for (int m0 = 0; m0 < p.M; m0 += 8) {
     v4u uv[8][J];
 #pragma unroll
@@ -851,26 +853,43 @@ __device__ __forceinline__ void st_router_shared(const Params &p, const Ctx &cx,
   const int Nsh = 2 * p.Is;
   const int TS = (Nsh >> 4) * (p.h / p.pl.kc_sh13);
   const int J = (p.pl.kc_router + 511) >> 9;
-  if (p.ho >= 2) {
-    // hand-off: every row's u is out
-    const int c = bid() & 7;
-    ho_wait(p.sync, kHoU + c, hb[kHoU + c] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+  // hand-off: every row's u is out (a router task waits once its weights are on their way)
+  bool waited = p.ho < 2;
+  auto wait_u = [&] {
+    if (!waited) {
+      const int c = bid() & 7;
+      ho_wait(p.sync, kHoU + c, hb[kHoU + c] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+      waited = true;
+    }
+  };
+  // narrow: a shared gate/up task's first weights are on their way before the wait too
+  // (its wave then takes a row's top-k sooner)
+  PreA pf = pre_none();
+  if constexpr (NARROW) {
+    if (cx.gw >= TR && cx.gw < TR + TS) {
+      Ctx cs = cx;
+      cs.gw = cx.gw - TR;
+      linear_prefetch<kW8B128>(linear_prefetch_addr<kW8B128>(cs, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13),
+                               pf);
+    }
   }
   // (narrow: at most one task per wave, which the host checks)
   for (int t = cx.gw; t < TR + TS; t += NARROW ? 1 << 30 : cx.nw) {
     if (t < TR) {
       const int e = t % p.E, c = t / p.E;
       if (J == 1)
-        router_task_j<1>(p, w.w_router, u, e, c, cx.lane);
+        router_task_j<1>(p, w.w_router, u, e, c, cx.lane, wait_u);
       else
-        router_task_j<2>(p, w.w_router, u, e, c, cx.lane);
+        router_task_j<2>(p, w.w_router, u, e, c, cx.lane, wait_u);
       if (p.ho >= 2) ho_count(p.sync, kHoRt + (t & 7), cx.lane);
     } else {
+      wait_u();
       linear_task<kW8B128, NARROW ? 1 : 3>(t - TR, cx.lane, w.sh_w13, nullptr, w.sh_w13_s, Nsh, p.h, p.pl.kc_sh13, u,
-                                           p.M, p.s.p_sh);
+                                           p.M, p.s.p_sh, &pf, NARROW && pf.on);
       if (p.ho >= 2) ho_count(p.sync, kHoSh + ((t - TR) & 7), cx.lane);
     }
   }
+  wait_u();
   if (p.a8) st_u_quant(p, cx, u);
 }
 
