@@ -358,7 +358,7 @@ struct SyncWords {
   unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
   unsigned tq[64][16];      // wo_a tasks finished per 32-column group of t; only grow
   unsigned cb[128][16];     // down-stage waves finished per 32-column group of the MoE output; only grow
-  unsigned ho[136][64];     // producer hand-off counters (kHo* below); only grow
+  unsigned ho[144][64];     // producer hand-off counters (kHo* below); only grow
   unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };
@@ -373,10 +373,11 @@ enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 //   kHoQb + h: wq_b tasks of head h; kHoAtt + h: attention items of head h;
 //   kHoWq / kHoWkv: wqkv tasks of the q / kv latent columns (task counters);
 //   kHoTb + c: quantized t groups of wo_b's K chunk c; kHoWb: wo_b tasks (task counter);
-//   kHoU: MoE input rows; kHoRt / kHoSh: router and shared gate/up tasks (task counters).
+//   kHoU: MoE input rows; kHoRt / kHoSh: router and shared gate/up tasks (task counters);
+//   kHoX: the attention input's normalized rows (row counter).
 enum : int {
   kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoWq = 73, kHoWkv = 81, kHoTb = 89, kHoWb = 97, kHoU = 105,
-  kHoRt = 113, kHoSh = 121, kHoSlots = 129, kHoHeads = 32, kHoTbChunks = 8
+  kHoRt = 113, kHoSh = 121, kHoX = 129, kHoSlots = 137, kHoHeads = 32, kHoTbChunks = 8
 };
 
 // Waits until counter id reaches target (modular, like the barrier's release word): lane 0
@@ -476,6 +477,43 @@ __device__ __forceinline__ void grid_barrier_meet(SyncWords *sw, unsigned nblock
     *next = r + 1u;
   }
   __syncthreads();
+}
+
+// The arrival half of a grid barrier (thread bt, after a __syncthreads that follows what
+// the arrival stands for): the block counts itself for barrier *next and goes on; the
+// barrier completes, as grid_barrier_meet's, when every block has arrived.  *fence takes
+// the barrier's number for grid_fence_wait.
+__device__ __forceinline__ void grid_barrier_arrive(SyncWords *sw, unsigned nblocks, unsigned *next, unsigned *fence) {
+  const unsigned grp = blockIdx.x & 7u;
+  const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
+  const unsigned per = (nblocks - grp + 7u) / 8u;
+  const unsigned r = *next;
+  const unsigned a = __hip_atomic_fetch_add(gptr(&sw->group[grp][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a == per * r - 1u) {
+    const unsigned b = __hip_atomic_fetch_add(gptr(&sw->top[0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (b == ngroups * r - 1u)
+      for (unsigned g = 0; g < ngroups; g++)
+        __hip_atomic_store(gptr(&sw->release[g][0]), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  *fence = r;
+  *next = r + 1u;
+}
+
+// Waits (lane 0; the wave follows) until barrier r has completed, i.e. every block has
+// arrived at it; bounded like the barrier's own spin.
+__device__ __forceinline__ void grid_fence_wait(SyncWords *sw, unsigned r, int lane) {
+  if (lane == 0) {
+    unsigned spins = 0;
+    while ((int)(__hip_atomic_load(gptr(&sw->release[blockIdx.x & 7u][0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                 r) < 0) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1u << 24)) {
+        __hip_atomic_fetch_or(gptr(&sw->health), (unsigned)kFaultBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace dsl

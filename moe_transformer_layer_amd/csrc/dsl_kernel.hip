@@ -55,9 +55,13 @@ __device__ __forceinline__ void key_offsets_row(const Params &p, const dsl_kv &k
 }
 
 // RMSNorm of the layer input, then MXFP8 quantization (kept as exact bf16 values).
+// With `fence` (hand-offs in place of the grid barrier after this stage) each row is
+// counted on the eight copies of kHoX once its stores have drained and every block has
+// arrived at barrier `fence` (so every block has read the counters' starting values).
 template <int E>
 __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const dsl_kv &kv,
-                                               const uint16_t *xin, float *red) {
+                                               const uint16_t *xin, float *red, bool count = false,
+                                               unsigned fence = 0u) {
   const int n = p.h, k = tid() * E;
   const bool act = k < n;
   // with fewer than 3 M blocks the key records of row m are resolved here, by block M + m
@@ -82,6 +86,15 @@ __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weight
     for (int e = 0; e < E; e++) v[e] = act ? v[e] * r * gm[e] : 0.f;
     mx_quant_dequant<E>(v);
     if (act) store_bf16<E>(p.s.xb + (size_t)m * n + k, v);
+    if (count) {
+      barrier_drain();
+      __syncthreads();
+      if (tid() < kWave) {
+        grid_fence_wait(p.sync, fence, tid());
+        if (tid() < 8)
+          __hip_atomic_fetch_add(gptr(&p.sync->ho[kHoX + tid()][0]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -200,7 +213,7 @@ __device__ __forceinline__ void kvpost_row(const Params &p, const dsl_weights &w
 // NARROW: the narrow-step kernel (q rank 1024, head dim 512: 2 and 1 elements per thread)
 template <bool NARROW>
 __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &w, const dsl_kv &kv, float *red,
-                                            uint8_t *tmp, const unsigned *hb, int l) {
+                                            uint8_t *tmp, const unsigned *hb, int l, bool fenced, unsigned fence) {
   const int eq = NARROW ? 2 : row_elems(p.qr), ekv = NARROW ? 1 : row_elems(p.D);
   // q of row m on block m, kv of row m on block M + m, row m's key offsets on block 2 M + m
   // (with fewer than 3 M blocks the key offsets come from the norm stage, with fewer than
@@ -242,9 +255,12 @@ __device__ __forceinline__ void st_qkv_post(const Params &p, const dsl_weights &
     }
     if (p.ho && b < 3 * p.M) {
       // hand-off: the row's stores drained in every wave, then one count (a q row on all
-      // eight copies of its counter; a kv record or a key-offset row on kHoKv)
+      // eight copies of its counter; a kv record or a key-offset row on kHoKv).  A key-offset
+      // row waits on nothing else, so with `fence` it first waits for every block's arrival
+      // (the counters' starting values read everywhere).
       barrier_drain();
       __syncthreads();
+      if (fenced && b >= 2 * p.M && tid() < kWave) grid_fence_wait(p.sync, fence, tid());
       if (tid() < (b < p.M ? 8 : 1))
         __hip_atomic_fetch_add(gptr(&p.sync->ho[b < p.M ? kHoQ + tid() : kHoKv][0]), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -644,11 +660,17 @@ __device__ __forceinline__ void st_wo_a_fold(const Params &p, const Ctx &cx, con
 }
 
 // wqkv with the hand-offs: count each finished task for its part (q or kv latent columns)
+// (wait_x: the rows come by hand-off, kHoX, instead of a grid barrier)
 template <int MAXG, bool ONE>
-__device__ __forceinline__ void st_wqkv_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf) {
+__device__ __forceinline__ void st_wqkv_ho(const Params &p, const Ctx &cx, const dsl_weights &w, const PreA &pf,
+                                           bool wait_x, const unsigned *hb, int l) {
   const int N = p.qr + p.D, K = p.h, kc = p.pl.kc_qkv, ntile = N >> 4, T = ntile * (K / kc);
   int t = cx.gw;
   if (t >= T) return;
+  if (wait_x) {
+    const int c = bid() & 7;
+    ho_wait(p.sync, kHoX + c, hb[kHoX + c] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+  }
   linear_task<kW8T32, MAXG>(t, cx.lane, w.wqkv, w.wqkv_s, nullptr, N, K, kc, p.s.xb, p.M, p.s.p_qkv, &pf, pf.on);
   ho_count(p.sync, (((t % ntile) << 4) < p.qr ? kHoWq : kHoWkv) + (t & 7), cx.lane);
   if constexpr (ONE) return;
@@ -1676,6 +1698,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   const unsigned nb = gridDim.x;
   __shared__ unsigned ho_base[kHoSlots];         // hand-off counters before this launch
   __shared__ unsigned rt_flag;                   // layer + 1 once this block has seen every router task
+  __shared__ unsigned bar_fence;                 // the barrier every block arrives at once it has read the bases
   int mode, n_layers, a8, ho, Mrows;
   SyncWords *sw;
   Tracer tr;
@@ -1701,6 +1724,12 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   // full hand-offs (ho >= 2) also replace the barriers after wqkv, wo_b, the FFN norm and
   // (steps whose top-k runs in every block, bf16 expert inputs) the router
   const bool ho2 = ho >= 2, ho_router = ho2 && Mrows <= kTopkInBlockRows && !a8;
+  // the grid barrier after the attention-input norm is replaced by a row hand-off too
+  // (with a block for every q, kv and key-offset row): its other role, that no block reads
+  // a counter's starting value after a producer has counted on it, passes to an early
+  // arrival of every block at a barrier that the first producers (the norm rows and the
+  // key-offset rows, which wait on nothing else) wait for before counting
+  const bool fenced = ho2 && (int)nb >= 3 * Mrows;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
     const bool last = l == n_layers - 1;
@@ -1722,24 +1751,36 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
                                  : 0u;
           cb_base[cx.wave] = cb_read_base(p, cx);
         }
+        if (fenced && l == 0) {
+          __syncthreads();  // this block's starting values are all read (ho_base, tq_base, cb_base)
+          if (tid() == kBarrierThread) grid_barrier_arrive(sw, nb, &bar_next, &bar_fence);
+          __syncthreads();
+        }
+        const unsigned fence = bar_fence;
         const uint16_t *xin = A_.xin;
         if constexpr (NARROW) {
-          st_attn_norm_e<8>(p, w, kv, xin, red);
+          st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence);
         } else {
           switch (row_elems(p.h)) {
-            case 1: st_attn_norm_e<1>(p, w, kv, xin, red); break;
-            case 2: st_attn_norm_e<2>(p, w, kv, xin, red); break;
-            case 4: st_attn_norm_e<4>(p, w, kv, xin, red); break;
-            case 8: st_attn_norm_e<8>(p, w, kv, xin, red); break;
-            default: st_attn_norm_e<16>(p, w, kv, xin, red); break;
+            case 1: st_attn_norm_e<1>(p, w, kv, xin, red, fenced, fence); break;
+            case 2: st_attn_norm_e<2>(p, w, kv, xin, red, fenced, fence); break;
+            case 4: st_attn_norm_e<4>(p, w, kv, xin, red, fenced, fence); break;
+            case 8: st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence); break;
+            default: st_attn_norm_e<16>(p, w, kv, xin, red, fenced, fence); break;
           }
         }
       }
-      SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
+      if (fenced) {
+        linear_prefetch<kW8T32>(pa, pf_wqkv);
+        tr.mark();
+        tr.mark();
+      } else {
+        SYNC_PF(linear_prefetch<kW8T32>(pa, pf_wqkv));
+      }
       {
         STAGE(l);
         if (ho2)
-          st_wqkv_ho<NARROW ? 1 : 3, NARROW>(p, cx, w, pf_wqkv);
+          st_wqkv_ho<NARROW ? 1 : 3, NARROW>(p, cx, w, pf_wqkv, fenced, ho_base, l);
         else
           linear_all_pre<kW8T32, NARROW ? 1 : 3, NARROW>(cx, w.wqkv, w.wqkv_s, nullptr, p.qr + p.D, p.h, p.pl.kc_qkv, p.s.xb,
                                                  p.M, p.s.p_qkv, pf_wqkv);
@@ -1749,7 +1790,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       {
         STAGE(l);
         pa = linear_prefetch_addr<kW8T32>(cx, w.wq_b, w.wq_b_s, nullptr, p.H * p.D, p.qr, p.pl.kc_qb);
-        st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0], ho_base, l);
+        st_qkv_post<NARROW>(p, w, kv, red, &wave_lds[0][0], ho_base, l, fenced, bar_fence);
       }
       // With hand-offs ("Mono decode layer for DeepSeek-V4.1-Flash on MI355X", Design: the
       // stages pass data between CTAs through tagged flags) no grid barrier separates
