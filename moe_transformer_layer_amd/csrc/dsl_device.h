@@ -358,7 +358,7 @@ struct SyncWords {
   unsigned release[8][64];  // completed barriers: one copy per group, polled by that group
   unsigned tq[64][16];      // wo_a tasks finished per 32-column group of t; only grow
   unsigned cb[128][16];     // down-stage waves finished per 32-column group of the MoE output; only grow
-  unsigned ho[144][64];     // producer hand-off counters (kHo* below); only grow
+  unsigned ho[152][64];     // producer hand-off counters (kHo* below); only grow
   unsigned health;          // 0, or a DSL device fault code
   unsigned pad2[63];
 };
@@ -374,10 +374,11 @@ enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 //   kHoWq / kHoWkv: wqkv tasks of the q / kv latent columns (task counters);
 //   kHoTb + c: quantized t groups of wo_b's K chunk c; kHoWb: wo_b tasks (task counter);
 //   kHoU: MoE input rows; kHoRt / kHoSh: router and shared gate/up tasks (task counters);
-//   kHoX: the attention input's normalized rows (row counter).
+//   kHoX: the attention input's normalized rows (row counter); kHoO: the layer output's
+//   32-column groups (task counter), for the next chained layer.
 enum : int {
   kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoWq = 73, kHoWkv = 81, kHoTb = 89, kHoWb = 97, kHoU = 105,
-  kHoRt = 113, kHoSh = 121, kHoX = 129, kHoSlots = 137, kHoHeads = 32, kHoTbChunks = 8
+  kHoRt = 113, kHoSh = 121, kHoX = 129, kHoO = 137, kHoSlots = 145, kHoHeads = 32, kHoTbChunks = 8
 };
 
 // Waits until counter id reaches target (modular, like the barrier's release word): lane 0

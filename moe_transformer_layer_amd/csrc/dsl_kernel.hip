@@ -61,9 +61,18 @@ __device__ __forceinline__ void key_offsets_row(const Params &p, const dsl_kv &k
 template <int E>
 __device__ __forceinline__ void st_attn_norm_e(const Params &p, const dsl_weights &w, const dsl_kv &kv,
                                                const uint16_t *xin, float *red, bool count = false,
-                                               unsigned fence = 0u) {
+                                               unsigned fence = 0u, unsigned wait_out = 0u, const unsigned *hb = nullptr) {
   const int n = p.h, k = tid() * E;
   const bool act = k < n;
+  // a chained layer's input comes from the layer before by hand-off (wait_out: the count
+  // of its output's column groups to wait for), not across a grid barrier
+  if (wait_out && bid() < p.M) {
+    unsigned base = 0;
+#pragma unroll
+    for (int c = 0; c < 8; c++) base += hb[kHoO + c];
+    if (tid() < kWave) ho_wait_sum8(p.sync, kHoO, base + wait_out, tid());
+    __syncthreads();
+  }
   // with fewer than 3 M blocks the key records of row m are resolved here, by block M + m
   // (or by block m itself with fewer than 2 M blocks); else by the qkv_post stage
   const bool late = (int)gridDim.x >= 3 * p.M, split = (int)gridDim.x >= 2 * p.M;
@@ -1566,6 +1575,8 @@ __device__ __forceinline__ void cb_count_combine(const Params &p, const Ctx &cx,
     live[i] = moe_mode || (m < p.M && ldg(p.pos + m) >= 0);
   }
   cb_group_combine(p, R, moe_mode, last, dst, g, cx.lane, live);
+  // the group's output columns are out: count them for the next chained layer's input norm
+  if (p.ho >= 2 && !last) ho_count(p.sync, kHoO + (g & 7), cx.lane);
 }
 
 // Each wave's combine group counter, read before its block's first arrival (no down wave
@@ -1730,6 +1741,9 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   // arrival of every block at a barrier that the first producers (the norm rows and the
   // key-offset rows, which wait on nothing else) wait for before counting
   const bool fenced = ho2 && (int)nb >= 3 * Mrows;
+  // chained layers hand the layer output to the next layer's input norm when the combine
+  // is folded (its last waves count the output's column groups)
+  bool out_ho = false;
   tr.mark();
   for (int l = 0; l < n_layers; l++) {
     const bool last = l == n_layers - 1;
@@ -1758,15 +1772,18 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         }
         const unsigned fence = bar_fence;
         const uint16_t *xin = A_.xin;
+        // (layers after the first, when the one before handed its output off: its 32-column
+        // groups, counted per layer)
+        const unsigned wait_out = l > 0 && out_ho ? (unsigned)l * (unsigned)(p.h >> 5) : 0u;
         if constexpr (NARROW) {
-          st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence);
+          st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base);
         } else {
           switch (row_elems(p.h)) {
-            case 1: st_attn_norm_e<1>(p, w, kv, xin, red, fenced, fence); break;
-            case 2: st_attn_norm_e<2>(p, w, kv, xin, red, fenced, fence); break;
-            case 4: st_attn_norm_e<4>(p, w, kv, xin, red, fenced, fence); break;
-            case 8: st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence); break;
-            default: st_attn_norm_e<16>(p, w, kv, xin, red, fenced, fence); break;
+            case 1: st_attn_norm_e<1>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base); break;
+            case 2: st_attn_norm_e<2>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base); break;
+            case 4: st_attn_norm_e<4>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base); break;
+            case 8: st_attn_norm_e<8>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base); break;
+            default: st_attn_norm_e<16>(p, w, kv, xin, red, fenced, fence, wait_out, ho_base); break;
           }
         }
       }
@@ -1975,6 +1992,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
     {
       STAGE(l);
       cfold = NARROW || cb_fold(p);  // (likewise)
+      out_ho = fenced && cfold && !moe_mode;
       st_down<NARROW>(p, cx, w, R, wave_lds[cx.wave]);
       if (cfold) cb_count_combine(p, cx, R, moe_mode, last, A_.xout, cb_base);
     }
@@ -1986,7 +2004,15 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       }
     }
     if (!last) {
-      SYNC();
+      if (out_ho) {
+        // the next layer's input comes by hand-off (kHoO); the block's own waves still
+        // finish this layer before any starts the next (the LDS tables and areas are reused)
+        __syncthreads();
+        tr.mark();
+        tr.mark();
+      } else {
+        SYNC();
+      }
     }
     tr.mark();
   }
