@@ -1291,10 +1291,19 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
   __builtin_amdgcn_sched_barrier(0);
   valu_store_scales<Q>(sl, lane, scg);
   valu_store_scales<Q>(sl + 16 * NB, lane, scu);
+  // row r's scale bytes in LDS, read a row ahead of their use: read where they are used,
+  // each LDS round trip stood between two rows' arithmetic
+  auto sidx = [&](int r, int q) { return (r % G >= H ? 16 * NB : 0) + ((r / G) * H + r % H) * NB + lane + 64 * q; };
+  uint32_t sb[Q];
+#pragma unroll
+  for (int q = 0; q < Q; q++) sb[q] = sl[sidx(0, q)];
   float acc[16];
 #pragma unroll
   for (int r = 0; r < NR; r++) {
-    const int gi = r / G, rr = r % G, half = rr >= H ? 1 : 0, n = gi * H + rr % H;
+    const int gi = r / G, rr = r % G, half = rr >= H ? 1 : 0;
+    uint32_t sbn[Q];
+#pragma unroll
+    for (int q = 0; q < Q; q++) sbn[q] = r + 1 < NR ? (uint32_t)sl[sidx(r + 1, q)] : 0u;
     if (rr == 0) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[v] = 0.f;
@@ -1308,10 +1317,7 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
         ring[r % DEPTH][q] = ldw16(W + (size_t)row_of(r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
     }
 #pragma unroll
-    for (int q = 0; q < Q; q++) {
-      const float sc = e8m0_to_f32(sl[half * 16 * NB + n * NB + lane + 64 * q]);
-      valu_row<CE, Q>(cur[q], sc, xv[q], acc + (half * H + rr % H) * CE);
-    }
+    for (int q = 0; q < Q; q++) valu_row<CE, Q>(cur[q], e8m0_to_f32(sb[q]), xv[q], acc + (half * H + rr % H) * CE);
     if (rr == G - 1) {
       const float tot = wave_transpose_sum<16>(acc, lane);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
@@ -1322,6 +1328,8 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
         stg(p.s.zr + (size_t)(p0 + m) * I + tile * 16 + gi * H + rl, (uint16_t)f32_to_bf16(swiglu_clamp(tot, upv, p.lim)));
       }
     }
+#pragma unroll
+    for (int q = 0; q < Q; q++) sb[q] = sbn[q];
   }
 }
 
@@ -1355,10 +1363,17 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < NR / 16; b++) valu_store_scales<Q>(sl + 16 * NB * b, lane, sc[b]);
+  // (scale bytes read a row ahead of their use, as in the gate/up tasks)
+  uint32_t sb[Q];
+#pragma unroll
+  for (int q = 0; q < Q; q++) sb[q] = sl[lane + 64 * q];
   float acc[16];
 #pragma unroll
   for (int r = 0; r < NR; r++) {
     const int gi = r / G, rr = r % G;
+    uint32_t sbn[Q];
+#pragma unroll
+    for (int q = 0; q < Q; q++) sbn[q] = r + 1 < NR ? (uint32_t)sl[(r + 1) * NB + lane + 64 * q] : 0u;
     if (rr == 0) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[v] = 0.f;
@@ -1372,15 +1387,14 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
         ring[r % DEPTH][q] = ldw16(W + (size_t)(tile * NR + r + DEPTH) * row_bytes + 16 * (lane + 64 * q));
     }
 #pragma unroll
-    for (int q = 0; q < Q; q++) {
-      const float sc = e8m0_to_f32(sl[r * NB + lane + 64 * q]);
-      valu_row<CE, Q>(cur[q], sc, xv[q], acc + rr * CE);
-    }
+    for (int q = 0; q < Q; q++) valu_row<CE, Q>(cur[q], e8m0_to_f32(sb[q]), xv[q], acc + rr * CE);
     if (rr == G - 1) {
       const float tot = wave_transpose_sum<16>(acc, lane);
       const int j = lane >> 2;  // value (row, pair) = (j / CE, j % CE)
       if ((lane & 3) == 0 && j % CE < ce) stg(p.s.y + (size_t)(p0 + j % CE) * h + tile * NR + gi * G + j / CE, tot);
     }
+#pragma unroll
+    for (int q = 0; q < Q; q++) sb[q] = sbn[q];
   }
 }
 
