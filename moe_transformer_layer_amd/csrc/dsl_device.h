@@ -375,10 +375,11 @@ enum : unsigned { kFaultBarrier = 1u, kFaultSlot = 2u };
 //   kHoTb + c: quantized t groups of wo_b's K chunk c; kHoWb: wo_b tasks (task counter);
 //   kHoU: MoE input rows; kHoRt / kHoSh: router and shared gate/up tasks (task counters);
 //   kHoX: the attention input's normalized rows (row counter); kHoO: the layer output's
-//   32-column groups (task counter), for the next chained layer.
+//   32-column groups (task counter), for the next chained layer; kHoTk: rows whose experts
+//   the grid top-k has stored (steps wider than a block's waves).
 enum : int {
   kHoQ = 0, kHoKv = 8, kHoQb = 9, kHoAtt = 41, kHoWq = 73, kHoWkv = 81, kHoTb = 89, kHoWb = 97, kHoU = 105,
-  kHoRt = 113, kHoSh = 121, kHoX = 129, kHoO = 137, kHoSlots = 145, kHoHeads = 32, kHoTbChunks = 8
+  kHoRt = 113, kHoSh = 121, kHoX = 129, kHoO = 137, kHoTk = 145, kHoSlots = 146, kHoHeads = 32, kHoTbChunks = 8
 };
 
 // Waits until counter id reaches target (modular, like the barrier's release word): lane 0

@@ -1032,32 +1032,25 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     const int c0 = __popcll(R.rows[lane]), c1 = __popcll(R.rows[lane + 64]);
     R.cnt[lane] = c0;
     R.cnt[lane + 64] = c1;
-    int s0 = c0, s1 = c1;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int a0 = __shfl_up(s0, o, kWave), a1 = __shfl_up(s1, o, kWave);
-      if (lane >= o) {
-        s0 += a0; s1 += a1;
-      }
+    // exclusive prefix sums of the counts in expert order, by bit planes (a count is at
+    // most M): per plane one ballot, and the bits below the lane counted
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int s0 = 0, s1 = 0, tot0 = 0, tot1 = 0;
+    for (int b = 0; (1 << b) <= M; b++) {
+      const unsigned long long m0 = __ballot((c0 >> b) & 1), m1 = __ballot((c1 >> b) & 1);
+      s0 += __popcll(m0 & below) << b;
+      s1 += __popcll(m1 & below) << b;
+      tot0 += __popcll(m0) << b;
+      tot1 += __popcll(m1) << b;
     }
-    const int tot0 = __shfl(s0, kWave - 1, kWave);
-    R.start[lane] = s0 - c0;
-    R.start[lane + 64] = tot0 + s1 - c1;
-    const int tot1 = __shfl(s1, kWave - 1, kWave);
+    R.start[lane] = s0;
+    R.start[lane + 64] = tot0 + s1;
     if (lane == 0) R.np = tot0 + tot1;
     // the distinct experts: in id order for a step of at most 8 rows; wider steps take
     // the experts with more rows first (then by id), so that the round-robin task order
     // gives every wave an even share of the matrix-core experts
-    const unsigned long long below = (1ull << lane) - 1ull;
     int cmax = 0;
-    if (M > 8) {
-      cmax = c0 > c1 ? c0 : c1;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int t = __shfl_xor(cmax, o, kWave);
-        cmax = t > cmax ? t : cmax;
-      }
-    }
+    if (M > 8) cmax = (int)wave_max((float)(c0 > c1 ? c0 : c1));
     int at = 0;
     for (int c = cmax; c >= 0; c--) {
       // c = 0 takes every expert with rows (all of them in id order when M <= 8)
@@ -1749,6 +1742,10 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
   // full hand-offs (ho >= 2) also replace the barriers after wqkv, wo_b, the FFN norm and
   // (steps whose top-k runs in every block, bf16 expert inputs) the router
   const bool ho2 = ho >= 2, ho_router = ho2 && Mrows <= kTopkInBlockRows && !a8;
+  // no grid barrier after the router either when the top-k runs over the grid: its row
+  // waves wait for the router tasks' counts and count their rows, for which every block
+  // then waits
+  const bool ho_topk = ho2 && !a8;
   // the grid barrier after the attention-input norm is replaced by a row hand-off too
   // (with a block for every q, kv and key-offset row): its other role, that no block reads
   // a counter's starting value after a producer has counted on it, passes to an early
@@ -1945,7 +1942,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       if (moe_mode && l == 0 && cx.lane == 0) cb_base[cx.wave] = cb_read_base(p, cx);
       st_router_shared<NARROW>(p, cx, w, moe_mode ? p.x : p.s.u, ho_base, l);
     }
-    SYNC_IF(!ho_router);
+    SYNC_IF(!ho_topk);
     {
       STAGE(l);
       if (NARROW || p.M <= kTopkInBlockRows) {
@@ -1971,8 +1968,20 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
         tr.mark();
         tr.mark();
       } else {
+        if (ho_topk && cx.gw < p.M) {
+          ho_wait_sum8(p.sync, kHoRt, hb_sum8(ho_base, kHoRt) + (unsigned)(l + 1) * (unsigned)ho_t_rt(p), cx.lane);
+          asm volatile("" ::: "memory");  // the logit loads stay after the wait
+        }
         topk_in_grid(p, cx, moe_mode, last ? p.taps.logits : nullptr);
-        SYNC();
+        if (ho_topk) {
+          if (cx.gw < p.M) ho_count(p.sync, kHoTk, cx.lane);
+          if (cx.wave == 0) ho_wait(p.sync, kHoTk, ho_base[kHoTk] + (unsigned)(l + 1) * (unsigned)p.M, cx.lane);
+          __syncthreads();
+          tr.mark();
+          tr.mark();
+        } else {
+          SYNC();
+        }
         topk_from_grid(p, R);
       }
       build_routing(p, cx, R);
@@ -1992,7 +2001,7 @@ __global__ void __launch_bounds__(kThreads, 1) dsl_layer_kernel(Params p_arg) {
       st_routed_gate_up<NARROW>(p, cx, w, R, p.a8 ? p.s.uq : moe_mode ? p.x : p.s.u, wave_lds[cx.wave]);
       // the shared SwiGLU, off the critical path: its reader, the shared down projection,
       // comes after the next grid barrier
-      st_shared_swiglu(p, moe_mode, ho_router, ho_base, l);
+      st_shared_swiglu(p, moe_mode, ho_topk, ho_base, l);
     }
     SYNC();
     if (a8) {
