@@ -749,9 +749,30 @@ __device__ __forceinline__ void mx_quant_dequant(float v[E]) {
   for (int e = 0; e < E; e++) am = fmaxf(am, fabsf(v[e]));
   if constexpr (E < 32) am = group_max<32 / E>(am);
   const uint32_t X = mx_e4m3_exponent(am);
-  const float inv = mx_inv_scale(X), sc = e8m0_to_f32(X);
+  const float sc = e8m0_to_f32(X);
+  if (X == 0u) {
+    // (a block of zeros or of values below 2^-118: its scale 2^-127 is subnormal, so the
+    // software rounding)
+    const float inv = mx_inv_scale(X);
 #pragma unroll
-  for (int e = 0; e < E; e++) v[e] = e4m3_to_f32(f32_to_e4m3(v[e] * inv)) * sc;
+    for (int e = 0; e < E; e++) v[e] = e4m3_to_f32(f32_to_e4m3(v[e] * inv)) * sc;
+  } else {
+    // gfx950's scaled conversions: v / 2^(X-127) to e4m3 with ties to even, and the codes
+    // back times 2^(X-127); the input is clamped to the block's e4m3 range first (past it
+    // the conversion gives the NaN code where the software rounding saturates).  Checked
+    // bit for bit against the software rounding on 4 M values with a pair probe, ties,
+    // subnormal steps, signed zeros and the saturation edge included.
+    const float lim = 448.0f * sc;
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      typedef short v2s __attribute__((ext_vector_type(2)));
+      const float a = fminf(fmaxf(v[e], -lim), lim), b = E > 1 ? fminf(fmaxf(v[e + 1 < E ? e + 1 : e], -lim), lim) : 0.f;
+      const v2s c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
+      const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((unsigned)(unsigned short)c[0], sc, false);
+      v[e] = d[0];
+      if (E > 1) v[e + 1 < E ? e + 1 : e] = d[1];
+    }
+  }
 }
 
 // Elements per thread for a row of n values spread over the block (a power of two).
