@@ -1049,10 +1049,10 @@ __device__ __forceinline__ void build_routing(const Params &p, const Ctx &cx, Ro
     // the distinct experts: in id order for a step of at most 8 rows; wider steps take
     // the experts with more rows first (then by id), so that the round-robin task order
     // gives every wave an even share of the matrix-core experts
-    int cmax = 0;
-    if (M > 8) cmax = (int)wave_max((float)(c0 > c1 ? c0 : c1));
+    const int cmax = (int)wave_max((float)(c0 > c1 ? c0 : c1));
+    if (lane == 0) R.cmax = cmax;
     int at = 0;
-    for (int c = cmax; c >= 0; c--) {
+    for (int c = M > 8 ? cmax : 0; c >= 0; c--) {
       // c = 0 takes every expert with rows (all of them in id order when M <= 8)
       const bool in0 = c > 0 ? c0 == c : (M <= 8 && c0 > 0), in1 = c > 0 ? c1 == c : (M <= 8 && c1 > 0);
       const unsigned long long b0 = __ballot(in0), b1 = __ballot(in1);
@@ -1245,18 +1245,20 @@ __device__ __forceinline__ void valu_store_scales(uint8_t *dst, int lane, const 
 
 constexpr int kValuDepth = 16;  // weight rows in flight per wave
 
-// Gate/up of one expert for its CE <= 2 rows over a tile of 16 gate and 16 up rows,
-// SwiGLU in the epilogue.  Rows are taken in groups of G = 16 / CE (half gate, half up)
-// so one butterfly sums a group's 16 outputs; gate totals land in lanes 0-31, the
-// matching up totals 32 lanes higher.
-template <int CE, int Q>
+// Gate/up of one expert for its CE <= 2 rows over a tile of NR / 2 gate and NR / 2 up
+// rows (NR = 32, or 16 for tiles of 8 columns), SwiGLU in the epilogue.  Rows are taken
+// in groups of G = 16 / CE (half gate, half up) so one butterfly sums a group's 16
+// outputs; gate totals land in lanes 0-31, the matching up totals 32 lanes higher.
+template <int CE, int Q, int NR = 32>
 __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_weights &w, const Routing &R,
                                                     const uint16_t *u, int e, int p0, int ce, int tile, int lane,
                                                     uint8_t *sl) {
   constexpr int NB = 64 * Q;   // 32-blocks per weight row
   constexpr int G = 16 / CE;   // rows per group
   constexpr int H = G / 2;     // gate (and up) rows per group
-  constexpr int NR = 32;       // rows per task
+  constexpr int TW = NR / 2;   // gate (and up) rows per task: the tile's columns
+  constexpr int SC = NR * Q / 32;  // 1 KB scale chunks per half (TW rows of NB bytes)
+  static_assert(NR % G == 0 && SC >= 1, "tile shape");
   constexpr int DEPTH = kValuDepth / Q;
   const int h = p.h, I = p.I;
   const size_t row_bytes = (size_t)h >> 1;
@@ -1267,13 +1269,13 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
   for (int m = 0; m < CE; m++) rows[m] = u + (size_t)R.pair_row[p0 + (m < ce ? m : 0)] * h;
   uint32_t xv[Q][CE][16];
   valu_load_x<CE, Q>(rows, lane, xv);
-  v4u scg[Q], scu[Q];
-  valu_load_scales<Q>(S + (size_t)(tile * 16) * NB, lane, scg);
-  valu_load_scales<Q>(S + (size_t)(I + tile * 16) * NB, lane, scu);
+  v4u scg[SC], scu[SC];
+  valu_load_scales<SC>(S + (size_t)(tile * TW) * NB, lane, scg);
+  valu_load_scales<SC>(S + (size_t)(I + tile * TW) * NB, lane, scu);
   // weight row r of the task in processing order: group r / G, gate rows then up rows
   auto row_of = [&](int r) -> int {
     const int gi = r / G, rr = r % G;
-    return (rr >= H ? I : 0) + tile * 16 + gi * H + rr % H;
+    return (rr >= H ? I : 0) + tile * TW + gi * H + rr % H;
   };
   v4u ring[DEPTH][Q];
   __builtin_amdgcn_sched_barrier(0);
@@ -1282,11 +1284,11 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
 #pragma unroll
     for (int q = 0; q < Q; q++) ring[r][q] = ldw16(W + (size_t)row_of(r) * row_bytes + 16 * (lane + 64 * q));
   __builtin_amdgcn_sched_barrier(0);
-  valu_store_scales<Q>(sl, lane, scg);
-  valu_store_scales<Q>(sl + 16 * NB, lane, scu);
+  valu_store_scales<SC>(sl, lane, scg);
+  valu_store_scales<SC>(sl + TW * NB, lane, scu);
   // row r's scale bytes in LDS, read a row ahead of their use: read where they are used,
   // each LDS round trip stood between two rows' arithmetic
-  auto sidx = [&](int r, int q) { return (r % G >= H ? 16 * NB : 0) + ((r / G) * H + r % H) * NB + lane + 64 * q; };
+  auto sidx = [&](int r, int q) { return (r % G >= H ? TW * NB : 0) + ((r / G) * H + r % H) * NB + lane + 64 * q; };
   uint32_t sb[Q];
 #pragma unroll
   for (int q = 0; q < Q; q++) sb[q] = sl[sidx(0, q)];
@@ -1318,7 +1320,7 @@ __device__ __forceinline__ void routed_gate_up_valu(const Params &p, const dsl_w
       const int j = lane >> 2;  // value (half, row, activation row) = (j >> 3, (j & 7) / CE, (j & 7) % CE)
       const int rl = (j & 7) / CE, m = (j & 7) % CE;
       if (lane < 32 && (lane & 3) == 0 && m < ce) {
-        stg(p.s.zr + (size_t)(p0 + m) * I + tile * 16 + gi * H + rl, (uint16_t)f32_to_bf16(swiglu_clamp(tot, upv, p.lim)));
+        stg(p.s.zr + (size_t)(p0 + m) * I + tile * TW + gi * H + rl, (uint16_t)f32_to_bf16(swiglu_clamp(tot, upv, p.lim)));
       }
     }
 #pragma unroll
@@ -1397,9 +1399,12 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
 template <bool NARROW>
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                   const uint16_t *u, uint8_t *sl) {
-  const int tiles_n = p.I >> 4;
-  const int T = R.nd * tiles_n;
   const int qv = NARROW ? 2 : p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
+  // every expert on the VALU path at K = 4096: tiles of 8 columns (32 KB tasks, twice as
+  // many), so that a last round of tasks that only some waves get ends twice as soon
+  const bool halves = qv == 2 && R.cmax <= 2;
+  const int tiles_n = p.I >> (halves ? 3 : 4);
+  const int T = R.nd * tiles_n;
   for (int t = cx.gw; t < T; t += cx.nw) {
     // wave-uniform: keep them (and the addresses built on them) in scalar registers
     const int tu = __builtin_amdgcn_readfirstlane(t);
@@ -1411,6 +1416,9 @@ __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx
       if (!NARROW && qv == 1) {
         if (ce == 1) routed_gate_up_valu<1, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
         else routed_gate_up_valu<2, 1>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+      } else if (halves) {
+        if (ce == 1) routed_gate_up_valu<1, 2, 16>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
+        else routed_gate_up_valu<2, 2, 16>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
       } else {
         if (ce == 1) routed_gate_up_valu<1, 2>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);
         else routed_gate_up_valu<2, 2>(p, w, R, u, e, p0, ce, tile, cx.lane, sl);

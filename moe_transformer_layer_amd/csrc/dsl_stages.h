@@ -98,7 +98,8 @@ struct Routing {
   unsigned long long rows[128];    // rows that selected each expert (bit m)
   int cnt[128], start[128], list[128];
   int nd;
-  int np;  // (row, slot) pairs routed (live rows times k)
+  int np;    // (row, slot) pairs routed (live rows times k)
+  int cmax;  // the most rows any expert has
 };
 
 struct Ctx {
