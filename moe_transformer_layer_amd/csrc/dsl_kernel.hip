@@ -1393,15 +1393,16 @@ __device__ __forceinline__ void routed_down_valu(const Params &p, const dsl_weig
   }
 }
 
-// Routed gate/up tasks (selected expert, 16-row tile of gate and of up): task t to wave t mod
-// waves.
+// Routed gate/up tasks (selected expert, tile of 16 or 8 rows of gate and of up): task t
+// to wave t mod waves.
 // NARROW: hidden 4096 and at most 8 rows (one 16-row group).
 template <bool NARROW>
 __device__ __forceinline__ void st_routed_gate_up(const Params &p, const Ctx &cx, const dsl_weights &w, const Routing &R,
                                   const uint16_t *u, uint8_t *sl) {
   const int qv = NARROW ? 2 : p.h == 2048 ? 1 : p.h == 4096 ? 2 : 0;  // VALU path: K = 2048 q
   // every expert on the VALU path at K = 4096: tiles of 8 columns (32 KB tasks, twice as
-  // many), so that a last round of tasks that only some waves get ends twice as soon
+  // many).  A last round of tasks that only some waves get then ends twice as soon, and
+  // the finer tasks measured faster than splitting only that round.
   const bool halves = qv == 2 && R.cmax <= 2;
   const int tiles_n = p.I >> (halves ? 3 : 4);
   const int T = R.nd * tiles_n;
